@@ -1,0 +1,13 @@
+"""MI355X (gfx950) MoE route-count / dispatch / combine.
+
+The compute path lives in libmoe_route.so (hand-written HIP kernels behind a
+C ABI, declared in include/moe_route.h); this package is its thin Python
+binding.  Import is cheap: the library is loaded on first use and its absence
+raises instead of falling back to anything else.
+"""
+from ._lib import (DedupOut, DedupPlan, DispatchOut, MoeError, combine, dedup_dispatch, dispatch,
+                   fp8_dequant, load, route_count, version, workspace, workspace_size)
+
+__all__ = ["DedupOut", "DedupPlan", "DispatchOut", "MoeError", "combine", "dedup_dispatch",
+           "dispatch", "fp8_dequant", "load", "route_count", "version", "workspace",
+           "workspace_size"]

@@ -1,0 +1,423 @@
+// api.cpp - the C ABI of libmoe_route.so: argument checks, workspace carving
+// and the launch sequence of each entry point.  Every check runs before the
+// first launch, so a call that returns an error has enqueued nothing.
+#include <hip/hip_runtime_api.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "../../include/moe_route.h"
+#include "internal.hpp"
+
+#define MOE_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local std::string g_last_error;
+
+constexpr int kTile = 1024;  // entries per routing tile (matches the rank kernel)
+constexpr int64_t kMaxRows = INT32_MAX;
+
+int fail(int status, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+int ok() { return MOE_OK; }
+
+int hip_fail(hipError_t e, const char* where) {
+    return fail(MOE_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+int elem_bytes(moe_dtype d) { return d == MOE_F32 ? 4 : (d == MOE_BF16 ? 2 : 1); }
+
+// Workspace carving.  Sizes depend only on (T, K, E, R).
+struct Carve {
+    size_t total = 0;
+    size_t take(size_t bytes) {
+        const size_t at = total;
+        total += align256(bytes);
+        return at;
+    }
+};
+
+struct RouteWs {  // one routing level: N entries over NK keys
+    size_t local_rank, tile_cnt, tile_flags, off;
+    int64_t tiles;
+};
+
+RouteWs carve_route(Carve& c, int64_t N, int NK) {
+    RouteWs r;
+    r.tiles = (N + kTile - 1) / kTile;
+    r.local_rank = c.take(sizeof(int32_t) * (size_t)(N > 0 ? N : 1));
+    r.tile_cnt = c.take(sizeof(int32_t) * (size_t)(r.tiles > 0 ? r.tiles : 1) * NK);
+    r.tile_flags = c.take(sizeof(int32_t) * 2 * (size_t)(r.tiles > 0 ? r.tiles : 1));
+    r.off = c.take(sizeof(int32_t) * ((size_t)NK + 1));
+    return r;
+}
+
+struct Layout {
+    RouteWs experts, ranks;
+    size_t total;
+};
+
+Layout layout(int64_t T, int K, int E, int R) {
+    Carve c;
+    Layout L;
+    L.experts = carve_route(c, T * K, E);
+    if (R > 0) L.ranks = carve_route(c, T * R, R);
+    L.total = c.total;
+    return L;
+}
+
+template <typename P>
+P* at(void* ws, size_t off) {
+    return (P*)((char*)ws + off);
+}
+
+int check_routing(int64_t T, int K, int E, const int32_t* idx) {
+    if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T=%lld must be >= 0", (long long)T);
+    if (K < 1 || K > 16) return fail(MOE_ERR_INVALID_ARG, "K=%d must be in [1,16]", K);
+    if (E < 1 || E > 1024) return fail(MOE_ERR_INVALID_ARG, "E=%d must be in [1,1024]", E);
+    if (T * (int64_t)K >= ((int64_t)1 << 31))
+        return fail(MOE_ERR_INVALID_ARG, "T*K=%lld must be < 2^31", (long long)(T * K));
+    if (T > 0 && !idx) return fail(MOE_ERR_INVALID_ARG, "idx is NULL");
+    if (idx && !aligned(idx, 4)) return fail(MOE_ERR_INVALID_ARG, "idx is not 4-byte aligned");
+    return MOE_OK;
+}
+
+int check_ws(void* ws, size_t ws_bytes, size_t need) {
+    if (ws_bytes < need)
+        return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
+                    ws_bytes, need);
+    if (need > 0 && !ws) return fail(MOE_ERR_WORKSPACE, "workspace is NULL");
+    if (ws && !aligned(ws, 256)) return fail(MOE_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+    return MOE_OK;
+}
+
+int check_rows_ptr(const void* p, int64_t rows, const char* name) {
+    if (rows > 0 && !p) return fail(MOE_ERR_INVALID_ARG, "%s is NULL", name);
+    if (p && !aligned(p, 16)) return fail(MOE_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+    return MOE_OK;
+}
+
+int check_H(int64_t H, bool fp8) {
+    if (H <= 0 || H % 8 != 0)
+        return fail(MOE_ERR_INVALID_ARG, "H=%lld must be a positive multiple of 8", (long long)H);
+    if (fp8 && H % 128 != 0)
+        return fail(MOE_ERR_INVALID_ARG, "H=%lld must be a multiple of 128 for fp8",
+                    (long long)H);
+    if (H > ((int64_t)1 << 24))
+        return fail(MOE_ERR_INVALID_ARG, "H=%lld exceeds 2^24", (long long)H);
+    return MOE_OK;
+}
+
+#define MOE_TRY(expr)                 \
+    do {                              \
+        const int st_ = (expr);       \
+        if (st_ != MOE_OK) return st_; \
+    } while (0)
+
+#define MOE_HIP(expr, where)                  \
+    do {                                      \
+        const hipError_t e_ = (expr);         \
+        if (e_ != hipSuccess) return hip_fail(e_, where); \
+    } while (0)
+
+// Rank pass + scan pass for one routing level.
+struct LevelOut {
+    int32_t* cnt_out = nullptr;
+    int32_t* off_out = nullptr;
+    int32_t* packed_cnt = nullptr;
+    int32_t* packed_off = nullptr;
+    int32_t* stats = nullptr;
+};
+
+hipError_t route_level(void* ws, const RouteWs& L, moe::KeyKind kind, const int32_t* idx,
+                       const int32_t* rank_slot, int64_t N, int K, int E, int R, int NK,
+                       int64_t cap, int64_t rows_limit, const LevelOut& o, moe::StatsMode mode,
+                       hipStream_t s) {
+    moe::RankArgs ra;
+    ra.kind = kind;
+    ra.idx = idx;
+    ra.rank_slot = rank_slot;
+    ra.N = N;
+    ra.K = K;
+    ra.E = E;
+    ra.R = R;
+    ra.NK = NK;
+    ra.local_rank = at<int32_t>(ws, L.local_rank);
+    ra.tile_cnt = at<int32_t>(ws, L.tile_cnt);
+    ra.tile_flags = at<int32_t>(ws, L.tile_flags);
+    hipError_t e = moe::launch_rank(ra, s);
+    if (e != hipSuccess) return e;
+    moe::ScanArgs sa;
+    sa.tile_cnt = ra.tile_cnt;
+    sa.tile_flags = ra.tile_flags;
+    sa.tiles = (int)L.tiles;
+    sa.NK = NK;
+    sa.cap = cap;
+    sa.rows_limit = rows_limit;
+    sa.off_ws = at<int32_t>(ws, L.off);
+    sa.cnt_out = o.cnt_out;
+    sa.off_out = o.off_out;
+    sa.packed_cnt = o.packed_cnt;
+    sa.packed_off = o.packed_off;
+    sa.stats = o.stats;
+    sa.mode = mode;
+    return moe::launch_scan(sa, s);
+}
+
+moe::SlotArgs slot_args(void* ws, const RouteWs& L, const int32_t* idx, int K, int E, int64_t cap,
+                        int64_t packed_rows) {
+    moe::SlotArgs a;
+    a.idx = idx;
+    a.local_rank = at<int32_t>(ws, L.local_rank);
+    a.tile_base = at<int32_t>(ws, L.tile_cnt);
+    a.off = at<int32_t>(ws, L.off);
+    a.K = K;
+    a.E = E;
+    a.cap = cap;
+    a.packed_rows = packed_rows;
+    return a;
+}
+
+}  // namespace
+
+MOE_API int moe_version(void) { return (1 << 16) | 0; }
+
+MOE_API const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+MOE_API size_t moe_workspace_size(int64_t T, int K, int E, int R) {
+    if (T < 0 || K < 1 || E < 1 || R < 0) return 0;
+    return layout(T, K, E, R).total;
+}
+
+MOE_API int moe_route_count(const int32_t* idx, int64_t T, int K, int E, int32_t* cnt,
+                            int32_t* off, int32_t* stats, void* ws, size_t ws_bytes,
+                            void* stream) {
+    MOE_TRY(check_routing(T, K, E, idx));
+    if (!cnt || !off) return fail(MOE_ERR_INVALID_ARG, "cnt and off must be non-NULL");
+    const Layout L = layout(T, K, E, 0);
+    MOE_TRY(check_ws(ws, ws_bytes, L.total));
+    LevelOut o;
+    o.cnt_out = cnt;
+    o.off_out = off;
+    o.stats = stats;
+    MOE_HIP(route_level(ws, L.experts, moe::KeyKind::Experts, idx, nullptr, T * K, K, E, 0, E, 0,
+                        INT64_MAX, o, moe::StatsMode::Plain, (hipStream_t)stream),
+            "moe_route_count");
+    return ok();
+}
+
+MOE_API int moe_dispatch(const void* x, moe_dtype x_dt, int64_t T, int64_t H, const int32_t* idx,
+                         int K, int E, int64_t cap, int64_t packed_rows, void* packed_x,
+                         moe_dtype packed_dt, float* packed_scales, int32_t* packed_cnt,
+                         int32_t* packed_off, int32_t* packed_src, int64_t* tok_map,
+                         int32_t* stats, void* ws, size_t ws_bytes, void* stream) {
+    MOE_TRY(check_routing(T, K, E, idx));
+    if (x_dt != MOE_BF16 && x_dt != MOE_F32)
+        return fail(MOE_ERR_INVALID_ARG, "x dtype must be MOE_BF16 or MOE_F32");
+    const bool fp8 = packed_dt == MOE_FP8_E4M3;
+    if (packed_dt != x_dt && !fp8)
+        return fail(MOE_ERR_INVALID_ARG, "packed dtype must equal x dtype or be MOE_FP8_E4M3");
+    if (fp8 && x_dt != MOE_BF16)
+        return fail(MOE_ERR_UNSUPPORTED, "fp8 packing is implemented for bf16 input only");
+    MOE_TRY(check_H(H, fp8));
+    if (cap < 0) return fail(MOE_ERR_INVALID_ARG, "cap must be >= 0");
+    if (packed_rows < 0 || packed_rows > kMaxRows)
+        return fail(MOE_ERR_INVALID_ARG, "packed_rows must be in [0, 2^31-1]");
+    MOE_TRY(check_rows_ptr(x, T, "x"));
+    MOE_TRY(check_rows_ptr(packed_x, packed_rows, "packed_x"));
+    if (fp8 && packed_rows > 0 && !packed_scales)
+        return fail(MOE_ERR_INVALID_ARG, "packed_scales is NULL for fp8");
+    if (!fp8 && packed_scales)
+        return fail(MOE_ERR_INVALID_ARG, "packed_scales must be NULL unless fp8");
+    if (packed_scales && !aligned(packed_scales, 4))
+        return fail(MOE_ERR_INVALID_ARG, "packed_scales is not 4-byte aligned");
+    if (!packed_cnt) return fail(MOE_ERR_INVALID_ARG, "packed_cnt is NULL");
+    if (packed_rows > 0 && !packed_src) return fail(MOE_ERR_INVALID_ARG, "packed_src is NULL");
+    if (T > 0 && !tok_map) return fail(MOE_ERR_INVALID_ARG, "tok_map is NULL");
+    if (tok_map && !aligned(tok_map, 8)) return fail(MOE_ERR_INVALID_ARG, "tok_map is not 8-byte aligned");
+    const Layout L = layout(T, K, E, 0);
+    MOE_TRY(check_ws(ws, ws_bytes, L.total));
+    hipStream_t s = (hipStream_t)stream;
+
+    LevelOut o;
+    o.packed_cnt = packed_cnt;
+    o.packed_off = packed_off;
+    o.stats = stats;
+    MOE_HIP(route_level(ws, L.experts, moe::KeyKind::Experts, idx, nullptr, T * K, K, E, 0, E, cap,
+                        packed_rows, o, moe::StatsMode::Plain, s),
+            "moe_dispatch routing");
+    moe::ScatterArgs sa;
+    sa.slot = slot_args(ws, L.experts, idx, K, E, cap, packed_rows);
+    sa.x = x;
+    sa.T = T;
+    sa.H = H;
+    sa.x_bytes = elem_bytes(x_dt);
+    sa.fp8 = fp8;
+    sa.packed = packed_x;
+    sa.scales = packed_scales;
+    sa.packed_src = packed_src;
+    sa.tok_map = tok_map;
+    MOE_HIP(moe::launch_scatter(sa, s), "moe_dispatch scatter");
+    return ok();
+}
+
+MOE_API int moe_combine(const void* y, moe_dtype y_dt, int64_t y_rows, int64_t H,
+                        const int64_t* tok_map, const float* w, int64_t T, int K, int E,
+                        const moe_dedup_plan* dd, void* out, moe_dtype out_dt,
+                        float* out_weights, void* stream) {
+    if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T must be >= 0");
+    if (K < 1 || K > 16) return fail(MOE_ERR_INVALID_ARG, "K=%d must be in [1,16]", K);
+    if (y_dt != MOE_BF16 && y_dt != MOE_F32)
+        return fail(y_dt == MOE_FP8_E4M3 ? MOE_ERR_UNSUPPORTED : MOE_ERR_INVALID_ARG,
+                    "y dtype must be MOE_BF16 or MOE_F32");
+    if (out_dt != MOE_BF16 && out_dt != MOE_F32)
+        return fail(MOE_ERR_INVALID_ARG, "out dtype must be MOE_BF16 or MOE_F32");
+    MOE_TRY(check_H(H, false));
+    if (y_rows < 0) return fail(MOE_ERR_INVALID_ARG, "y_rows must be >= 0");
+    MOE_TRY(check_rows_ptr(y, y_rows, "y"));
+    MOE_TRY(check_rows_ptr(out, T, "out"));
+    if (T > 0 && (!tok_map || !w)) return fail(MOE_ERR_INVALID_ARG, "tok_map and w must be non-NULL");
+    if (tok_map && !aligned(tok_map, 8)) return fail(MOE_ERR_INVALID_ARG, "tok_map is not 8-byte aligned");
+    if (w && !aligned(w, 4)) return fail(MOE_ERR_INVALID_ARG, "w is not 4-byte aligned");
+    if (out_weights && !aligned(out_weights, 4))
+        return fail(MOE_ERR_INVALID_ARG, "out_weights is not 4-byte aligned");
+    moe::CombineArgs a{};
+    if (dd) {
+        if (E < 1 || E > 1024) return fail(MOE_ERR_INVALID_ARG, "E=%d must be in [1,1024]", E);
+        if (dd->R < 1 || dd->R > 32 || E % dd->R != 0)
+            return fail(MOE_ERR_INVALID_ARG, "R=%d must be in [1,32] and divide E=%d", dd->R, E);
+        if (T > 0 && (!dd->idx || !dd->rank_slot))
+            return fail(MOE_ERR_INVALID_ARG, "dedup plan idx and rank_slot must be non-NULL");
+        if (dd->recv_rows < 0 || dd->recv_rows > kMaxRows)
+            return fail(MOE_ERR_INVALID_ARG, "recv_rows must be in [0, 2^31-1]");
+        if (dd->partial && !aligned(dd->partial, 16))
+            return fail(MOE_ERR_INVALID_ARG, "partial is not 16-byte aligned");
+        a.R = dd->R;
+        a.idx = dd->idx;
+        a.rank_slot = dd->rank_slot;
+        a.recv_rows = dd->recv_rows;
+        a.partial = dd->partial;
+    }
+    a.y = y;
+    a.y_f32 = y_dt == MOE_F32;
+    a.y_rows = y_rows;
+    a.H = H;
+    a.tok_map = tok_map;
+    a.w = w;
+    a.T = T;
+    a.K = K;
+    a.E = E;
+    a.out = out;
+    a.out_f32 = out_dt == MOE_F32;
+    a.out_weights = out_weights;
+    MOE_HIP(moe::launch_combine(a, (hipStream_t)stream), "moe_combine");
+    return ok();
+}
+
+MOE_API int moe_dedup_dispatch(const void* x, moe_dtype x_dt, int64_t T, int64_t H,
+                               const int32_t* idx, int K, int E, int R, void* recv_x,
+                               int64_t recv_rows, int32_t* recv_cnt, int32_t* recv_off,
+                               int32_t* recv_src, int32_t* rank_slot, int64_t cap,
+                               int64_t packed_rows, void* packed_x, int32_t* packed_cnt,
+                               int32_t* packed_off, int32_t* packed_src, int64_t* tok_map,
+                               int32_t* stats, void* ws, size_t ws_bytes, void* stream) {
+    MOE_TRY(check_routing(T, K, E, idx));
+    if (R < 1 || R > 32 || E % R != 0)
+        return fail(MOE_ERR_INVALID_ARG, "R=%d must be in [1,32] and divide E=%d", R, E);
+    if (T * (int64_t)R >= ((int64_t)1 << 31))
+        return fail(MOE_ERR_INVALID_ARG, "T*R must be < 2^31");
+    if (x_dt != MOE_BF16 && x_dt != MOE_F32)
+        return fail(MOE_ERR_INVALID_ARG, "x dtype must be MOE_BF16 or MOE_F32");
+    MOE_TRY(check_H(H, false));
+    if (cap < 0) return fail(MOE_ERR_INVALID_ARG, "cap must be >= 0");
+    if (packed_rows < 0 || packed_rows > kMaxRows)
+        return fail(MOE_ERR_INVALID_ARG, "packed_rows must be in [0, 2^31-1]");
+    if (recv_rows < 0 || recv_rows > kMaxRows)
+        return fail(MOE_ERR_INVALID_ARG, "recv_rows must be in [0, 2^31-1]");
+    MOE_TRY(check_rows_ptr(x, T, "x"));
+    MOE_TRY(check_rows_ptr(recv_x, recv_rows, "recv_x"));
+    MOE_TRY(check_rows_ptr(packed_x, packed_rows, "packed_x"));
+    if (!recv_cnt || !recv_off || !packed_cnt)
+        return fail(MOE_ERR_INVALID_ARG, "recv_cnt, recv_off and packed_cnt must be non-NULL");
+    if (recv_rows > 0 && !recv_src) return fail(MOE_ERR_INVALID_ARG, "recv_src is NULL");
+    if (packed_rows > 0 && !packed_src) return fail(MOE_ERR_INVALID_ARG, "packed_src is NULL");
+    if (T > 0 && (!tok_map || !rank_slot))
+        return fail(MOE_ERR_INVALID_ARG, "tok_map and rank_slot must be non-NULL");
+    if (tok_map && !aligned(tok_map, 8)) return fail(MOE_ERR_INVALID_ARG, "tok_map is not 8-byte aligned");
+    const Layout L = layout(T, K, E, R);
+    MOE_TRY(check_ws(ws, ws_bytes, L.total));
+    hipStream_t s = (hipStream_t)stream;
+    const int xb = elem_bytes(x_dt);
+
+    // stage 1 routing: (token, rank) pairs, one recv row each, in token order per rank
+    LevelOut ro;
+    ro.cnt_out = recv_cnt;
+    ro.off_out = recv_off;
+    ro.stats = stats;
+    MOE_HIP(route_level(ws, L.ranks, moe::KeyKind::Ranks, idx, nullptr, T * R, K, E, R, R, 0,
+                        recv_rows, ro, moe::StatsMode::RecvRows, s),
+            "moe_dedup_dispatch rank routing");
+    moe::RecvArgs rc;
+    rc.x = x;
+    rc.T = T;
+    rc.H = H;
+    rc.x_bytes = xb;
+    rc.R = R;
+    rc.local_rank = at<int32_t>(ws, L.ranks.local_rank);
+    rc.tile_base = at<int32_t>(ws, L.ranks.tile_cnt);
+    rc.off = at<int32_t>(ws, L.ranks.off);
+    rc.recv_rows = recv_rows;
+    rc.recv_x = recv_x;
+    rc.recv_src = recv_src;
+    rc.rank_slot = rank_slot;
+    MOE_HIP(moe::launch_recv_copy(rc, s), "moe_dedup_dispatch recv copy");
+
+    // stage 2 routing: surviving entries to expert slots, then local expansion
+    LevelOut eo;
+    eo.packed_cnt = packed_cnt;
+    eo.packed_off = packed_off;
+    eo.stats = stats;
+    MOE_HIP(route_level(ws, L.experts, moe::KeyKind::Survivors, idx, rank_slot, T * K, K, E, R, E,
+                        cap, packed_rows, eo, moe::StatsMode::Experts, s),
+            "moe_dedup_dispatch expert routing");
+    moe::ExpandArgs ea;
+    ea.slot = slot_args(ws, L.experts, idx, K, E, cap, packed_rows);
+    ea.T = T;
+    ea.H = H;
+    ea.x_bytes = xb;
+    ea.R = R;
+    ea.rank_slot = rank_slot;
+    ea.recv_x = recv_x;
+    ea.packed = packed_x;
+    ea.packed_src = packed_src;
+    ea.tok_map = tok_map;
+    MOE_HIP(moe::launch_expand(ea, s), "moe_dedup_dispatch expansion");
+    return ok();
+}
+
+MOE_API int moe_fp8_dequant(const uint8_t* q, const float* scales, int64_t rows, int64_t H,
+                            void* y, void* stream) {
+    if (rows < 0) return fail(MOE_ERR_INVALID_ARG, "rows must be >= 0");
+    MOE_TRY(check_H(H, true));
+    MOE_TRY(check_rows_ptr(q, rows, "q"));
+    MOE_TRY(check_rows_ptr(y, rows, "y"));
+    if (rows > 0 && !scales) return fail(MOE_ERR_INVALID_ARG, "scales is NULL");
+    if (scales && !aligned(scales, 4)) return fail(MOE_ERR_INVALID_ARG, "scales is not 4-byte aligned");
+    MOE_HIP(moe::launch_fp8_dequant(q, scales, rows, H, y, (hipStream_t)stream), "moe_fp8_dequant");
+    return ok();
+}

@@ -1,0 +1,120 @@
+// device_common.hpp - gfx950 device helpers shared by the MoE route kernels:
+// wave64 ballot matching, DPP reductions, bf16 / OCP e4m3 conversions and
+// 16-byte vector memory access.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+// Entries per routing tile: 4 waves x 4 chunks x 64 lanes.
+constexpr int kTileWaves = 4;
+constexpr int kTileChunks = 4;
+constexpr int kTile = kTileWaves * kTileChunks * kWave;
+constexpr int kRankThreads = kTileWaves * kWave;
+
+constexpr int kFp8Block = 128;
+constexpr float kE4m3Max = 448.0f;
+
+// Key codes produced by the routing key functions.
+constexpr int kKeySkip = -1;     // "no expert": skipped, not counted
+constexpr int kKeyInvalid = -2;  // id outside [0, E) other than -1: counted invalid
+constexpr int kKeyDropped = -3;  // valid entry dropped before slotting: counted dropped
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// wave64 primitives
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ uint64_t ballot64(bool p) { return __ballot(p); }
+
+// Number of set bits of m in the lanes below the calling lane.
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Mask of the lanes whose key equals the calling lane's key (keys >= 0 only;
+// lanes with a negative key get an empty mask).  One ballot per key bit, so the
+// cost does not depend on how many distinct keys the wave holds.
+__device__ __forceinline__ uint64_t match_key(int key, int nbits) {
+    uint64_t m = ballot64(key >= 0);
+    for (int b = 0; b < nbits; ++b) {
+        const bool bit = (key >> b) & 1;
+        const uint64_t bm = ballot64(bit);
+        m &= bit ? bm : ~bm;
+    }
+    return key >= 0 ? m : 0ull;
+}
+
+template <typename T>
+__device__ __forceinline__ T readlane(T v, int lane) {
+    static_assert(sizeof(T) == 4, "32-bit readlane");
+    int r = __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane);
+    return __builtin_bit_cast(T, r);
+}
+
+// Max over each aligned group of 8 lanes (DPP quad permutes, then the half-row mirror).
+__device__ __forceinline__ float group8_max(float v) {
+    int iv = __builtin_bit_cast(int, v);
+    float o = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(iv, 0xB1, 0xF, 0xF, true));
+    v = fmaxf(v, o);
+    iv = __builtin_bit_cast(int, v);
+    o = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(iv, 0x4E, 0xF, 0xF, true));
+    v = fmaxf(v, o);
+    iv = __builtin_bit_cast(int, v);
+    o = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(iv, 0x141, 0xF, 0xF, true));
+    return fmaxf(v, o);
+}
+
+// ---------------------------------------------------------------------------
+// number formats
+// ---------------------------------------------------------------------------
+
+// Low / high bf16 of a packed pair, widened exactly to f32.
+__device__ __forceinline__ float bf16lo(uint32_t d) { return __builtin_bit_cast(float, d << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t d) {
+    return __builtin_bit_cast(float, d & 0xffff0000u);
+}
+
+// Two f32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    const uint32_t a = __builtin_bit_cast(uint16_t, (__bf16)lo);
+    const uint32_t b = __builtin_bit_cast(uint16_t, (__bf16)hi);
+    return a | (b << 16);
+}
+
+// Four f32 (each |v| <= 448) -> four OCP e4m3fn bytes, round to nearest even.
+__device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
+    int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
+    return (uint32_t)r;
+}
+
+// Two e4m3fn bytes (byte pair `hi` of d) -> f32, exact.
+template <bool HI>
+__device__ __forceinline__ void unpack_e4m3x2(uint32_t d, float& a, float& b) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    f2 v = __builtin_amdgcn_cvt_pk_f32_fp8((int)d, HI);
+    a = v.x;
+    b = v.y;
+}
+
+// ---------------------------------------------------------------------------
+// 16-byte memory access
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *(const u32x4*)p; }
+__device__ __forceinline__ u32x4 ld16_stream(const void* p) {
+    return __builtin_nontemporal_load((const u32x4*)p);
+}
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *(u32x4*)p = v; }
+__device__ __forceinline__ void st16_stream(void* p, u32x4 v) {
+    __builtin_nontemporal_store(v, (u32x4*)p);
+}
+
+}  // namespace moe

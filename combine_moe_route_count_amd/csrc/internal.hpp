@@ -1,0 +1,133 @@
+// internal.hpp - host-side launch interface between the C ABI layer (api.cpp)
+// and the kernel translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// routing: per-tile stable ranks, then the scan over tiles and keys
+// ---------------------------------------------------------------------------
+
+// Which key function maps a flat entry to its key.
+enum class KeyKind {
+    Experts,    // f = t*K + k, key = idx[f] when valid
+    Ranks,      // f = t*R + r, key = r when r is in token t's rank mask
+    Survivors,  // f = t*K + k, key = idx[f] when valid and its recv row exists
+};
+
+struct RankArgs {
+    KeyKind kind;
+    const int32_t* idx;
+    const int32_t* rank_slot;  // Survivors only
+    int64_t N;                 // entries (T*K or T*R)
+    int K, E, R;
+    int NK;                    // number of keys (E or R)
+    int32_t* local_rank;       // [N]  stable rank inside the tile, -1 for no key
+    int32_t* tile_cnt;         // [tiles][NK]
+    int32_t* tile_flags;       // [tiles][2]  invalid ids, dropped-before-slot
+};
+hipError_t launch_rank(const RankArgs& a, hipStream_t s);
+
+enum class StatsMode { Plain = 0, RecvRows = 1, Experts = 2 };
+
+struct ScanArgs {
+    int32_t* tile_cnt;          // [tiles][NK] counts in, exclusive per-key tile bases out
+    const int32_t* tile_flags;  // [tiles][2]
+    int tiles, NK;
+    int64_t cap;                // > 0: padded segments of cap rows
+    int64_t rows_limit;         // rows available (packed_rows / recv_rows)
+    int32_t* off_ws;            // [NK+1] offsets, always written (read by the copy kernels)
+    int32_t* cnt_out;           // [NK]   may be null
+    int32_t* off_out;           // [NK+1] may be null
+    int32_t* packed_cnt;        // [NK]   may be null
+    int32_t* packed_off;        // [NK+1] may be null
+    int32_t* stats;             // [3]    may be null
+    StatsMode mode;
+};
+hipError_t launch_scan(const ScanArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// row movement
+// ---------------------------------------------------------------------------
+
+struct SlotArgs {             // how an entry finds its packed row
+    const int32_t* idx;
+    const int32_t* local_rank;
+    const int32_t* tile_base;  // [tiles][E]
+    const int32_t* off;        // [E+1]
+    int K, E;
+    int64_t cap, packed_rows;
+};
+
+struct ScatterArgs {
+    SlotArgs slot;
+    const void* x;             // [T,H]
+    int64_t T, H;
+    int x_bytes;               // 2 (bf16) or 4 (f32)
+    bool fp8;                  // pack bf16 -> e4m3 + scales
+    void* packed;
+    float* scales;
+    int32_t* packed_src;
+    int64_t* tok_map;
+};
+hipError_t launch_scatter(const ScatterArgs& a, hipStream_t s);
+
+struct RecvArgs {             // dedup stage 1: one copy per (token, rank)
+    const void* x;
+    int64_t T, H;
+    int x_bytes;
+    int R;
+    const int32_t* local_rank;  // rank-level ranks [T*R]
+    const int32_t* tile_base;   // [tiles][R]
+    const int32_t* off;         // [R+1]
+    int64_t recv_rows;
+    void* recv_x;
+    int32_t* recv_src;
+    int32_t* rank_slot;
+};
+hipError_t launch_recv_copy(const RecvArgs& a, hipStream_t s);
+
+struct ExpandArgs {           // dedup stage 2: recv rows -> per-expert rows
+    SlotArgs slot;
+    int64_t T, H;
+    int x_bytes;
+    int R;
+    const int32_t* rank_slot;
+    const void* recv_x;
+    void* packed;
+    int32_t* packed_src;
+    int64_t* tok_map;
+};
+hipError_t launch_expand(const ExpandArgs& a, hipStream_t s);
+
+hipError_t launch_fp8_dequant(const uint8_t* q, const float* scales, int64_t rows, int64_t H,
+                              void* y, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// combine
+// ---------------------------------------------------------------------------
+
+struct CombineArgs {
+    const void* y;
+    bool y_f32;
+    int64_t y_rows, H;
+    const int64_t* tok_map;
+    const float* w;
+    int64_t T;
+    int K, E;
+    void* out;
+    bool out_f32;
+    float* out_weights;
+    // dedup (R == 0: plain)
+    int R;
+    const int32_t* idx;
+    const int32_t* rank_slot;
+    int64_t recv_rows;
+    float* partial;
+};
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,293 @@
+// route.hip - routing histogram, stable slot ranks and exclusive scans.
+//
+// The pages allocate dispatch slots with remote atomics ("Draft: cco + flydsl
+// dispatch/combine", ROCm/mori pull 448, PR description), which makes the slot
+// order depend on timing.  Here the slot of an entry is its rank among the
+// earlier entries of the same key in flat order (a stable counting sort), found
+// in two deterministic passes with no atomics on the result path:
+//
+//   rank pass  one workgroup per tile of kTile entries.  Each wave owns a
+//              contiguous quarter of the tile and walks it in 64-entry chunks.
+//              Lanes holding the same key are found with one ballot per key
+//              bit; a lane's rank inside its chunk is the count of equal-key
+//              lanes below it (mbcnt), plus the wave's running count for that
+//              key kept in LDS.  After a barrier each entry adds the counts of
+//              the tile's earlier waves.  Output: the rank inside the tile and
+//              the per-tile key counts.
+//   scan pass  one workgroup: exclusive scan over tiles per key (the tile
+//              bases), then over keys (the offsets, initial value 0 as in "Add
+//              standalone cuda.coop.cutlass package", NVIDIA/cccl pull 12311),
+//              then the per-key segment sizes under the capacity and the
+//              statistics.
+//
+// The wave-level ballot / prefix idea follows the wave64 prefix count that
+// "feat(EPv2): [preview] internode dispatch/combine over CCO/GDA" (ROCm/mori
+// pull 625, commit log) uses for slot assignment, computed here with mbcnt so
+// lane 0 needs no 64-bit shift.
+#include "device_common.hpp"
+#include "internal.hpp"
+
+namespace moe {
+
+namespace {
+
+struct ExpertKeys {
+    const int32_t* idx;
+    int E;
+    __device__ __forceinline__ int operator()(int64_t f) const {
+        const int32_t e = idx[f];
+        if (e >= 0 && e < E) return e;
+        return e == -1 ? kKeySkip : kKeyInvalid;
+    }
+};
+
+// f = t*R + r.  The rank of a valid expert e is e / (E/R); the division only
+// happens after the validity test so the -1 sentinel never lands on rank 0.
+struct RankKeys {
+    const int32_t* idx;
+    int K, E, R, er;
+    __device__ __forceinline__ int operator()(int64_t f) const {
+        const int t = (int)(f / R);
+        const int r = (int)(f - (int64_t)t * R);
+        uint32_t mask = 0;
+        for (int k = 0; k < K; ++k) {
+            const int32_t e = idx[(int64_t)t * K + k];
+            if (e >= 0 && e < E) mask |= 1u << (e / er);
+        }
+        return ((mask >> r) & 1u) ? r : kKeySkip;
+    }
+};
+
+// f = t*K + k: a valid expert keeps its key only if the recv row of its
+// (token, rank) exists; otherwise the entry is dropped before slotting.
+struct SurvivorKeys {
+    const int32_t* idx;
+    const int32_t* rank_slot;
+    int K, E, R, er;
+    __device__ __forceinline__ int operator()(int64_t f) const {
+        const int32_t e = idx[f];
+        if (!(e >= 0 && e < E)) return e == -1 ? kKeySkip : kKeyInvalid;
+        const int64_t t = f / K;
+        return rank_slot[t * R + e / er] >= 0 ? e : kKeyDropped;
+    }
+};
+
+template <class KeyFn>
+__global__ __launch_bounds__(kRankThreads) void rank_tiles_kernel(
+    KeyFn keys, int64_t N, int NK, int nbits, int32_t* __restrict__ local_rank,
+    int32_t* __restrict__ tile_cnt, int32_t* __restrict__ tile_flags) {
+    extern __shared__ int32_t run_all[];  // [kTileWaves][NK] running counts per wave
+    __shared__ int32_t flag_cnt[kTileWaves][2];
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave;
+    const int lane = tid % kWave;
+
+    for (int i = tid; i < kTileWaves * NK; i += kRankThreads) run_all[i] = 0;
+
+    const int64_t f0 = (int64_t)blockIdx.x * kTile + (int64_t)wave * (kTileChunks * kWave) + lane;
+    int key[kTileChunks];
+#pragma unroll
+    for (int c = 0; c < kTileChunks; ++c) {
+        const int64_t f = f0 + c * kWave;
+        key[c] = f < N ? keys(f) : kKeySkip;
+    }
+    __syncthreads();
+
+    int32_t* run = run_all + wave * NK;
+    int rank[kTileChunks];
+    int n_invalid = 0, n_dropped = 0;
+#pragma unroll
+    for (int c = 0; c < kTileChunks; ++c) {
+        const uint64_t m = match_key(key[c], nbits);
+        const int below = lanes_below(m);
+        int r = -1;
+        if (key[c] >= 0) r = run[key[c]] + below;
+        // the lowest lane of each equal-key group advances the wave's count
+        if (key[c] >= 0 && below == 0) run[key[c]] = r + __popcll(m);
+        rank[c] = r;
+        n_invalid += __popcll(ballot64(key[c] == kKeyInvalid));
+        n_dropped += __popcll(ballot64(key[c] == kKeyDropped));
+    }
+    if (lane == 0) {
+        flag_cnt[wave][0] = n_invalid;
+        flag_cnt[wave][1] = n_dropped;
+    }
+    __syncthreads();
+
+#pragma unroll
+    for (int c = 0; c < kTileChunks; ++c) {
+        const int64_t f = f0 + c * kWave;
+        if (f >= N) continue;
+        int r = rank[c];
+        if (key[c] >= 0)
+            for (int w = 0; w < wave; ++w) r += run_all[w * NK + key[c]];
+        local_rank[f] = r;
+    }
+    for (int e = tid; e < NK; e += kRankThreads) {
+        int s = 0;
+#pragma unroll
+        for (int w = 0; w < kTileWaves; ++w) s += run_all[w * NK + e];
+        tile_cnt[(int64_t)blockIdx.x * NK + e] = s;
+    }
+    if (tid == 0) {
+        int a = 0, b = 0;
+#pragma unroll
+        for (int w = 0; w < kTileWaves; ++w) {
+            a += flag_cnt[w][0];
+            b += flag_cnt[w][1];
+        }
+        tile_flags[2 * (int64_t)blockIdx.x] = a;
+        tile_flags[2 * (int64_t)blockIdx.x + 1] = b;
+    }
+}
+
+constexpr int kScanThreads = 1024;
+
+__global__ __launch_bounds__(kScanThreads) void scan_tiles_kernel(ScanArgs a) {
+    __shared__ int32_t part_sum[kScanThreads];
+    __shared__ int32_t buf[kScanThreads];
+    __shared__ int32_t red[2];
+    __shared__ int64_t red_drop;
+    const int tid = threadIdx.x;
+    const int NK = a.NK;
+    const int tiles = a.tiles;
+    int parts = kScanThreads / NK;
+    if (parts > tiles) parts = tiles;
+    if (parts < 1) parts = 1;
+    const bool active = tid < parts * NK;
+    const int key = tid % NK;
+    const int part = tid / NK;
+    const int tpp = (tiles + parts - 1) / parts;
+    const int t0 = part * tpp;
+    const int t1 = (t0 + tpp < tiles) ? t0 + tpp : tiles;
+
+    if (tid == 0) {
+        red[0] = 0;
+        red[1] = 0;
+        red_drop = 0;
+    }
+    // 1. per-part sums over its tile range
+    int32_t s = 0;
+    if (active)
+        for (int tl = t0; tl < t1; ++tl) s += a.tile_cnt[(int64_t)tl * NK + key];
+    part_sum[tid] = s;
+    __syncthreads();
+
+    // 2. rescan the range from the part's prefix: exclusive tile bases
+    int32_t total = 0;
+    if (active) {
+        int32_t run = 0;
+        for (int p = 0; p < part; ++p) run += part_sum[p * NK + key];
+        for (int tl = t0; tl < t1; ++tl) {
+            const int64_t i = (int64_t)tl * NK + key;
+            const int32_t c = a.tile_cnt[i];
+            a.tile_cnt[i] = run;
+            run += c;
+        }
+        if (part == parts - 1) total = run;
+    }
+    // 3. flags: invalid ids and entries dropped before slotting
+    {
+        int32_t fi = 0, fd = 0;
+        for (int tl = tid; tl < tiles; tl += kScanThreads) {
+            fi += a.tile_flags[2 * (int64_t)tl];
+            fd += a.tile_flags[2 * (int64_t)tl + 1];
+        }
+        __syncthreads();
+        if (fi) atomicAdd(&red[0], fi);
+        if (fd) atomicAdd(&red[1], fd);
+    }
+    // 4. exclusive scan of the per-key totals (Hillis-Steele over the block)
+    if (active && part == parts - 1) buf[key] = total;
+    if (tid >= NK) buf[tid] = 0;
+    __syncthreads();
+    const int32_t mine = buf[tid];
+    for (int d = 1; d < NK; d <<= 1) {
+        const int32_t add = tid >= d ? buf[tid - d] : 0;
+        __syncthreads();
+        buf[tid] += add;
+        __syncthreads();
+    }
+    const int32_t incl = buf[tid];
+    const int32_t excl = incl - mine;
+
+    // 5. offsets, segments under the capacity, dropped counts
+    if (tid < NK) {
+        const int64_t cnt = mine;
+        a.off_ws[tid] = excl;
+        if (a.cnt_out) a.cnt_out[tid] = mine;
+        if (a.off_out) a.off_out[tid] = excl;
+        const int64_t base = a.cap > 0 ? (int64_t)tid * a.cap : (int64_t)excl;
+        const int64_t seg = a.cap > 0 ? (cnt < a.cap ? cnt : a.cap) : cnt;
+        const int64_t lo = base < a.rows_limit ? base : a.rows_limit;
+        const int64_t end = base + seg;
+        const int64_t hi = end < a.rows_limit ? end : a.rows_limit;
+        const int64_t pc = hi > lo ? hi - lo : 0;
+        if (a.packed_cnt) a.packed_cnt[tid] = (int32_t)pc;
+        if (a.packed_off) a.packed_off[tid] = (int32_t)lo;
+        if (tid == NK - 1) {
+            a.off_ws[NK] = incl;
+            if (a.off_out) a.off_out[NK] = incl;
+            const int64_t bend = a.cap > 0 ? (int64_t)NK * a.cap : (int64_t)incl;
+            if (a.packed_off) a.packed_off[NK] = (int32_t)(bend < a.rows_limit ? bend : a.rows_limit);
+        }
+        if (cnt - pc) atomicAdd((unsigned long long*)&red_drop, (unsigned long long)(cnt - pc));
+    }
+    __syncthreads();
+    if (tid == 0 && a.stats) {
+        const int32_t dropped_slots = (int32_t)red_drop;
+        switch (a.mode) {
+            case StatsMode::Plain:
+                a.stats[0] = red[0];
+                a.stats[1] = red[1] + dropped_slots;
+                a.stats[2] = 0;
+                break;
+            case StatsMode::RecvRows:
+                a.stats[2] = dropped_slots;
+                break;
+            case StatsMode::Experts:
+                a.stats[0] = red[0];
+                a.stats[1] = red[1] + dropped_slots;
+                break;
+        }
+    }
+}
+
+int bits_for(int nk) {
+    int b = 0;
+    while ((1 << b) < nk) ++b;
+    return b;
+}
+
+}  // namespace
+
+hipError_t launch_rank(const RankArgs& a, hipStream_t s) {
+    const int64_t tiles = (a.N + kTile - 1) / kTile;
+    if (tiles == 0) return hipSuccess;
+    const size_t lds = sizeof(int32_t) * (size_t)kTileWaves * a.NK;
+    const int nbits = bits_for(a.NK);
+    switch (a.kind) {
+        case KeyKind::Experts:
+            rank_tiles_kernel<<<dim3((unsigned)tiles), dim3(kRankThreads), lds, s>>>(
+                ExpertKeys{a.idx, a.E}, a.N, a.NK, nbits, a.local_rank, a.tile_cnt, a.tile_flags);
+            break;
+        case KeyKind::Ranks:
+            rank_tiles_kernel<<<dim3((unsigned)tiles), dim3(kRankThreads), lds, s>>>(
+                RankKeys{a.idx, a.K, a.E, a.R, a.E / a.R}, a.N, a.NK, nbits, a.local_rank,
+                a.tile_cnt, a.tile_flags);
+            break;
+        case KeyKind::Survivors:
+            rank_tiles_kernel<<<dim3((unsigned)tiles), dim3(kRankThreads), lds, s>>>(
+                SurvivorKeys{a.idx, a.rank_slot, a.K, a.E, a.R, a.E / a.R}, a.N, a.NK, nbits,
+                a.local_rank, a.tile_cnt, a.tile_flags);
+            break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_scan(const ScanArgs& a, hipStream_t s) {
+    scan_tiles_kernel<<<dim3(1), dim3(kScanThreads), 0, s>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace moe

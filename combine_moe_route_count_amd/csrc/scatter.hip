@@ -1,0 +1,410 @@
+// scatter.hip - row movement of the dispatch: token rows into per-expert
+// packed rows (bit copies or the fused blockwise fp8 pack), the dedup recv copy
+// and local expansion, and the fp8 dequantize helper.
+//
+// One workgroup per source token.  The token row is loaded once into
+// registers with 16-byte loads (issued before the routing lookups, whose
+// latency they hide), then stored to each of the token's destination rows with
+// 16-byte stores, as the byte-generic row copy of "Draft: cco + flydsl
+// dispatch/combine" (ROCm/mori pull 448, PR description: 16 B scatter; commit
+// log: the dispatch copy is byte-generic, f32 works by element size) does on
+// its side.  The fp8 pack follows the coalesced blockwise quantize of the same
+// page (commit log, "Replace the lane-serial per-block quantize ..."): a
+// 128-element block lives in 8 adjacent lanes of 16 elements each, its amax is
+// a three-step DPP max inside the 8 lanes, and each lane stores its 16 fp8
+// bytes with one 16-byte store.
+#include "device_common.hpp"
+#include "internal.hpp"
+
+namespace moe {
+
+namespace {
+
+constexpr int kCopyThreads = 256;
+
+// Packed row of entry f, or -1 when the entry has no key or was dropped by the
+// capacity / row limit.
+__device__ __forceinline__ int entry_row(const SlotArgs& a, int64_t f) {
+    const int32_t lr = a.local_rank[f];
+    if (lr < 0) return -1;
+    const int32_t e = a.idx[f];
+    const int64_t slot = (int64_t)a.tile_base[(f / kTile) * a.E + e] + lr;
+    const int64_t base = a.cap > 0 ? (int64_t)e * a.cap : (int64_t)a.off[e];
+    if ((a.cap > 0 && slot >= a.cap) || base + slot >= a.packed_rows) return -1;
+    return (int)(base + slot);
+}
+
+template <int DMAX>
+__device__ __forceinline__ void broadcast_rows(int my_row, int (&rows)[DMAX]) {
+#pragma unroll
+    for (int d = 0; d < DMAX; ++d) rows[d] = readlane(my_row, d);
+}
+
+// Copy one row of nvec 16-byte vectors (already holding pass 0 in val) to up
+// to D destination rows; passes after the first reload from src.
+template <int DMAX, int VPT>
+__device__ __forceinline__ void store_row_copies(const char* src, int nvec, char* dst,
+                                                 int64_t row_bytes, const int (&rows)[DMAX], int D,
+                                                 u32x4 (&val)[VPT]) {
+    const int tid = threadIdx.x;
+    const int step = VPT * (int)blockDim.x;
+    for (int base = 0;;) {
+#pragma unroll
+        for (int d = 0; d < DMAX; ++d) {
+            if (d >= D) break;
+            if (rows[d] < 0) continue;
+            char* out = dst + (int64_t)rows[d] * row_bytes;
+#pragma unroll
+            for (int i = 0; i < VPT; ++i) {
+                const int v = base + tid + i * (int)blockDim.x;
+                if (v < nvec) st16(out + (int64_t)v * 16, val[i]);
+            }
+        }
+        base += step;
+        if (base >= nvec) break;
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int v = base + tid + i * (int)blockDim.x;
+            if (v < nvec) val[i] = ld16(src + (int64_t)v * 16);
+        }
+    }
+}
+
+template <int VPT>
+__device__ __forceinline__ void load_first_pass(const char* src, int nvec, u32x4 (&val)[VPT]) {
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+        const int v = threadIdx.x + i * (int)blockDim.x;
+        if (v < nvec) val[i] = ld16(src + (int64_t)v * 16);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// plain dispatch, bit copy (bf16 or f32)
+// ---------------------------------------------------------------------------
+template <int DMAX, int VPT>
+__global__ __launch_bounds__(kCopyThreads) void scatter_copy_kernel(ScatterArgs a) {
+    const int64_t t = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave;
+    const int K = a.slot.K;
+    const int64_t row_bytes = a.H * a.x_bytes;
+    const int nvec = (int)(row_bytes / 16);
+    const char* src = (const char*)a.x + t * row_bytes;
+
+    u32x4 val[VPT];
+    load_first_pass<VPT>(src, nvec, val);
+
+    int my_row = -1;
+    if (lane < K) my_row = entry_row(a.slot, t * K + lane);
+    if (tid < K) {
+        a.tok_map[t * K + tid] = my_row;
+        if (my_row >= 0) a.packed_src[my_row] = (int32_t)t;
+    }
+    int rows[DMAX];
+    broadcast_rows<DMAX>(my_row, rows);
+    store_row_copies<DMAX, VPT>(src, nvec, (char*)a.packed, row_bytes, rows, K, val);
+}
+
+// ---------------------------------------------------------------------------
+// plain dispatch, fused blockwise fp8 pack (bf16 in)
+// ---------------------------------------------------------------------------
+
+// Pack 16 bf16 values (two 16-byte vectors) of one lane; the 8 lanes of a
+// 128-element block agree on amax and the scale.
+__device__ __forceinline__ void fp8_pack16(const u32x4& lo, const u32x4& hi, u32x4& q,
+                                           float& scale) {
+    float v[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        v[2 * j] = bf16lo(lo[j]);
+        v[2 * j + 1] = bf16hi(lo[j]);
+        v[8 + 2 * j] = bf16lo(hi[j]);
+        v[8 + 2 * j + 1] = bf16hi(hi[j]);
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(v[j]));
+    amax = group8_max(amax);
+    scale = 1.0f;
+    if (amax > kE4m3Max) {
+        // q = e4m3(clamp((x * 448) / amax)); x * 448 is exact for bf16 x and the
+        // quotient is a correctly rounded f32 division.
+        scale = amax / kE4m3Max;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const float n = v[j] * kE4m3Max;
+            const float qv = n / amax;
+            v[j] = fminf(fmaxf(qv, -kE4m3Max), kE4m3Max);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        q[j] = pack_e4m3x4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]);
+}
+
+template <int DMAX, int UPT>
+__global__ __launch_bounds__(kCopyThreads) void scatter_fp8_kernel(ScatterArgs a) {
+    const int64_t t = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave;
+    const int K = a.slot.K;
+    const int64_t H = a.H;
+    const int nunits = (int)(H / 16);          // 16 elements per lane-unit
+    const int64_t nblk = H / kFp8Block;
+    const char* src = (const char*)a.x + t * H * 2;
+
+    int my_row = -1;
+    if (lane < K) my_row = entry_row(a.slot, t * K + lane);
+    if (tid < K) {
+        a.tok_map[t * K + tid] = my_row;
+        if (my_row >= 0) a.packed_src[my_row] = (int32_t)t;
+    }
+    int rows[DMAX];
+    for (int base = 0; base < nunits; base += UPT * (int)blockDim.x) {
+        u32x4 lo[UPT], hi[UPT];
+#pragma unroll
+        for (int i = 0; i < UPT; ++i) {
+            const int u = base + tid + i * (int)blockDim.x;
+            if (u < nunits) {
+                lo[i] = ld16(src + (int64_t)u * 32);
+                hi[i] = ld16(src + (int64_t)u * 32 + 16);
+            } else {
+                lo[i] = u32x4{0, 0, 0, 0};
+                hi[i] = u32x4{0, 0, 0, 0};
+            }
+        }
+        if (base == 0) broadcast_rows<DMAX>(my_row, rows);
+        u32x4 q[UPT];
+        float s[UPT];
+#pragma unroll
+        for (int i = 0; i < UPT; ++i) fp8_pack16(lo[i], hi[i], q[i], s[i]);
+#pragma unroll
+        for (int d = 0; d < DMAX; ++d) {
+            if (d >= K) break;
+            if (rows[d] < 0) continue;
+            char* out = (char*)a.packed + (int64_t)rows[d] * H;
+            float* sc = a.scales + (int64_t)rows[d] * nblk;
+#pragma unroll
+            for (int i = 0; i < UPT; ++i) {
+                const int u = base + tid + i * (int)blockDim.x;
+                if (u < nunits) {
+                    st16(out + (int64_t)u * 16, q[i]);
+                    if ((u & 7) == 0) sc[u >> 3] = s[i];
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dedup stage 1: one copy of x[t] per (t, r) in the token's rank mask
+// ---------------------------------------------------------------------------
+template <int DMAX, int VPT>
+__global__ __launch_bounds__(kCopyThreads) void recv_copy_kernel(RecvArgs a) {
+    const int64_t t = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave;
+    const int R = a.R;
+    const int64_t row_bytes = a.H * a.x_bytes;
+    const int nvec = (int)(row_bytes / 16);
+    const char* src = (const char*)a.x + t * row_bytes;
+
+    u32x4 val[VPT];
+    load_first_pass<VPT>(src, nvec, val);
+
+    int my_row = -1;
+    if (lane < R) {
+        const int64_t f = t * R + lane;
+        const int32_t lr = a.local_rank[f];
+        if (lr >= 0) {
+            const int64_t row = (int64_t)a.off[lane] + a.tile_base[(f / kTile) * R + lane] + lr;
+            my_row = row < a.recv_rows ? (int)row : -1;
+        }
+    }
+    if (tid < R) {
+        a.rank_slot[t * R + tid] = my_row;
+        if (my_row >= 0) a.recv_src[my_row] = (int32_t)t;
+    }
+    int rows[DMAX];
+    broadcast_rows<DMAX>(my_row, rows);
+    store_row_copies<DMAX, VPT>(src, nvec, (char*)a.recv_x, row_bytes, rows, R, val);
+}
+
+// ---------------------------------------------------------------------------
+// dedup stage 2: each recv row of token t expanded to the token's entries on
+// that rank (the same slots a plain dispatch of the surviving ids gives)
+// ---------------------------------------------------------------------------
+template <int KMAX, int VPT>
+__global__ __launch_bounds__(kCopyThreads) void expand_kernel(ExpandArgs a) {
+    const int64_t t = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave;
+    const int K = a.slot.K;
+    const int R = a.R;
+    const int er = a.slot.E / R;
+    const int64_t row_bytes = a.H * a.x_bytes;
+    const int nvec = (int)(row_bytes / 16);
+
+    int my_row = -1, my_rank = -1;
+    if (lane < K) {
+        const int64_t f = t * K + lane;
+        my_row = entry_row(a.slot, f);
+        if (my_row >= 0) my_rank = a.slot.idx[f] / er;
+    }
+    if (tid < K) {
+        a.tok_map[t * K + tid] = my_row;
+        if (my_row >= 0) a.packed_src[my_row] = (int32_t)t;
+    }
+    int rows[KMAX], ranks[KMAX];
+    broadcast_rows<KMAX>(my_row, rows);
+    broadcast_rows<KMAX>(my_rank, ranks);
+
+    for (int r = 0; r < R; ++r) {
+        bool any = false;
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) any |= (k < K) && ranks[k] == r && rows[k] >= 0;
+        if (!any) continue;
+        const int32_t srow = a.rank_slot[t * R + r];
+        const char* src = (const char*)a.recv_x + (int64_t)srow * row_bytes;
+        for (int base = 0; base < nvec; base += VPT * (int)blockDim.x) {
+            u32x4 val[VPT];
+#pragma unroll
+            for (int i = 0; i < VPT; ++i) {
+                const int v = base + tid + i * (int)blockDim.x;
+                if (v < nvec) val[i] = ld16(src + (int64_t)v * 16);
+            }
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k) {
+                if (k >= K) break;
+                if (ranks[k] != r || rows[k] < 0) continue;
+                char* out = (char*)a.packed + (int64_t)rows[k] * row_bytes;
+#pragma unroll
+                for (int i = 0; i < VPT; ++i) {
+                    const int v = base + tid + i * (int)blockDim.x;
+                    if (v < nvec) st16(out + (int64_t)v * 16, val[i]);
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fp8 dequantize: y = bf16(f32(q) * s[block])
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void fp8_dequant_kernel(const uint8_t* __restrict__ q,
+                                                          const float* __restrict__ scales,
+                                                          int64_t units, int64_t H,
+                                                          uint16_t* __restrict__ y) {
+    const int64_t upr = H / 16;
+    const int64_t nblk = H / kFp8Block;
+    for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < units;
+         u += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t row = u / upr;
+        const int64_t col = (u - row * upr) * 16;
+        const u32x4 v = ld16(q + row * H + col);
+        const float s = scales[row * nblk + col / kFp8Block];
+        u32x4 o0, o1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float a0, a1, b0, b1;
+            unpack_e4m3x2<false>(v[j], a0, a1);
+            unpack_e4m3x2<true>(v[j], b0, b1);
+            const uint32_t p0 = pack_bf16x2(a0 * s, a1 * s);
+            const uint32_t p1 = pack_bf16x2(b0 * s, b1 * s);
+            if (j < 2) {
+                o0[2 * j] = p0;
+                o0[2 * j + 1] = p1;
+            } else {
+                o1[2 * (j - 2)] = p0;
+                o1[2 * (j - 2) + 1] = p1;
+            }
+        }
+        st16(y + row * H + col, o0);
+        st16(y + row * H + col + 8, o1);
+    }
+}
+
+template <int VPT>
+int copy_threads(int nvec) {
+    int per = (nvec + VPT - 1) / VPT;
+    int th = ((per + kWave - 1) / kWave) * kWave;
+    if (th > kCopyThreads) th = kCopyThreads;
+    if (th < kWave) th = kWave;
+    return th;
+}
+
+template <template <int, int> class Launch, int VPT, class Args>
+hipError_t by_dmax(int D, dim3 grid, int threads, const Args& a, hipStream_t s) {
+    if (D <= 2) Launch<2, VPT>::go(grid, threads, a, s);
+    else if (D <= 4) Launch<4, VPT>::go(grid, threads, a, s);
+    else if (D <= 8) Launch<8, VPT>::go(grid, threads, a, s);
+    else if (D <= 16) Launch<16, VPT>::go(grid, threads, a, s);
+    else Launch<32, VPT>::go(grid, threads, a, s);
+    return hipGetLastError();
+}
+
+template <int D, int V>
+struct LaunchCopy {
+    static void go(dim3 g, int th, const ScatterArgs& a, hipStream_t s) {
+        scatter_copy_kernel<D, V><<<g, dim3(th), 0, s>>>(a);
+    }
+};
+template <int D, int V>
+struct LaunchFp8 {
+    static void go(dim3 g, int th, const ScatterArgs& a, hipStream_t s) {
+        scatter_fp8_kernel<D, V><<<g, dim3(th), 0, s>>>(a);
+    }
+};
+template <int D, int V>
+struct LaunchRecv {
+    static void go(dim3 g, int th, const RecvArgs& a, hipStream_t s) {
+        recv_copy_kernel<D, V><<<g, dim3(th), 0, s>>>(a);
+    }
+};
+template <int D, int V>
+struct LaunchExpand {
+    static void go(dim3 g, int th, const ExpandArgs& a, hipStream_t s) {
+        expand_kernel<D, V><<<g, dim3(th), 0, s>>>(a);
+    }
+};
+
+}  // namespace
+
+hipError_t launch_scatter(const ScatterArgs& a, hipStream_t s) {
+    if (a.T == 0) return hipSuccess;
+    const dim3 grid((unsigned)a.T);
+    if (a.fp8) {
+        const int nunits = (int)(a.H / 16);
+        const int th = copy_threads<2>(nunits);
+        return by_dmax<LaunchFp8, 2>(a.slot.K, grid, th, a, s);
+    }
+    const int nvec = (int)(a.H * a.x_bytes / 16);
+    const int th = copy_threads<4>(nvec);
+    return by_dmax<LaunchCopy, 4>(a.slot.K, grid, th, a, s);
+}
+
+hipError_t launch_recv_copy(const RecvArgs& a, hipStream_t s) {
+    if (a.T == 0) return hipSuccess;
+    const int nvec = (int)(a.H * a.x_bytes / 16);
+    return by_dmax<LaunchRecv, 4>(a.R, dim3((unsigned)a.T), copy_threads<4>(nvec), a, s);
+}
+
+hipError_t launch_expand(const ExpandArgs& a, hipStream_t s) {
+    if (a.T == 0) return hipSuccess;
+    const int nvec = (int)(a.H * a.x_bytes / 16);
+    return by_dmax<LaunchExpand, 4>(a.slot.K, dim3((unsigned)a.T), copy_threads<4>(nvec), a, s);
+}
+
+hipError_t launch_fp8_dequant(const uint8_t* q, const float* scales, int64_t rows, int64_t H,
+                              void* y, hipStream_t s) {
+    const int64_t units = rows * (H / 16);
+    if (units == 0) return hipSuccess;
+    int64_t blocks = (units + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    fp8_dequant_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(q, scales, units, H,
+                                                                    (uint16_t*)y);
+    return hipGetLastError();
+}
+
+}  // namespace moe

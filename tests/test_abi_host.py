@@ -1,0 +1,182 @@
+"""Host-only checks of the C ABI: the library loads, exports every function the
+header declares, sizes its workspace, and rejects bad arguments with the
+documented status before enqueueing anything.
+
+The calls run in a child process that sees no GPU (ROCR_VISIBLE_DEVICES=-1), so
+even a validation bug could not launch a kernel on a device."""
+import os
+import re
+import subprocess
+import sys
+import textwrap
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_route.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for n in ["moe_route_count", "moe_dispatch", "moe_combine", "moe_dedup_dispatch",
+              "moe_fp8_dequant", "moe_workspace_size", "moe_last_error", "moe_version"]:
+        assert n in names, n
+
+
+CHILD = textwrap.dedent(r"""
+import ctypes, json, sys
+sys.path.insert(0, ROOT)
+from combine_moe_route_count_amd import _lib as L
+lib = L.load()
+res = {}
+res["exports"] = {n: hasattr(lib, n) for n in NAMES}
+res["version"] = lib.moe_version()
+res["ws"] = [lib.moe_workspace_size(*a) for a in [(8192, 8, 256, 0), (8192, 8, 256, 0),
+             (16384, 6, 64, 8), (0, 1, 1, 0), (1, 16, 1024, 0), (-1, 8, 8, 0)]]
+P = ctypes.c_void_p
+A = P(0x100000)       # aligned stand-in pointers: never dereferenced, every case fails a check
+A8 = P(0x100008)
+A4 = P(0x100004)
+ws_need = lib.moe_workspace_size(100, 4, 16, 0)
+WS = P(0x200000)
+
+def disp(**kw):
+    a = dict(x=A, x_dt=0, T=100, H=64, idx=A, K=4, E=16, cap=0, rows=400, packed=A, pdt=0,
+             scales=None, pc=A, po=None, ps=A, tm=A, st=None, ws=WS, wsb=ws_need)
+    a.update(kw)
+    st = lib.moe_dispatch(a["x"], a["x_dt"], a["T"], a["H"], a["idx"], a["K"], a["E"], a["cap"],
+                          a["rows"], a["packed"], a["pdt"], a["scales"], a["pc"], a["po"], a["ps"],
+                          a["tm"], a["st"], a["ws"], a["wsb"], None)
+    return [st, lib.moe_last_error().decode()]
+
+res["dispatch"] = {
+    "K0": disp(K=0), "K17": disp(K=17), "E0": disp(E=0), "E1025": disp(E=1025),
+    "Tneg": disp(T=-1), "H12": disp(H=12), "Hzero": disp(H=0),
+    "fp8_H64": disp(pdt=2, scales=A, H=64),
+    "fp8_from_f32": disp(pdt=2, x_dt=1, scales=A, H=128),
+    "fp8_no_scales": disp(pdt=2, H=128),
+    "scales_not_fp8": disp(scales=A),
+    "dtype_mix": disp(pdt=1),
+    "bad_dtype": disp(x_dt=7),
+    "x_null": disp(x=None), "x_unaligned": disp(x=A8), "packed_unaligned": disp(packed=A8),
+    "idx_null": disp(idx=None), "tok_map_null": disp(tm=None), "tok_map_unaligned": disp(tm=A4),
+    "pc_null": disp(pc=None), "ps_null": disp(ps=None),
+    "cap_neg": disp(cap=-1), "rows_neg": disp(rows=-1), "rows_huge": disp(rows=1 << 31),
+    "TK_overflow": disp(T=1 << 28, K=16),
+    "ws_small": disp(wsb=ws_need - 1), "ws_null": disp(ws=None),
+    "ws_unaligned": disp(ws=P(0x200010)),
+}
+
+def comb(**kw):
+    a = dict(y=A, ydt=0, yr=10, H=64, tm=A, w=A, T=5, K=2, E=8, dd=None, out=A, odt=0, ow=None)
+    a.update(kw)
+    st = lib.moe_combine(a["y"], a["ydt"], a["yr"], a["H"], a["tm"], a["w"], a["T"], a["K"], a["E"],
+                         a["dd"], a["out"], a["odt"], a["ow"], None)
+    return [st, lib.moe_last_error().decode()]
+
+bad_plan = L.DedupPlan(3, 0x100000, 0x100000, 10, None)
+res["combine"] = {
+    "K0": comb(K=0), "H7": comb(H=7), "y_fp8": comb(ydt=2), "out_fp8": comb(odt=2),
+    "y_null": comb(y=None), "tm_null": comb(tm=None), "w_null": comb(w=None),
+    "out_unaligned": comb(out=A8), "y_rows_neg": comb(yr=-1),
+    "dd_R_not_divisor": comb(dd=ctypes.byref(bad_plan)),
+}
+
+def dd(**kw):
+    a = dict(x=A, xdt=1, T=50, H=64, idx=A, K=6, E=64, R=8, rx=A, rr=300, rc=A, ro=A, rs=A, rsl=A,
+             cap=0, pr=300, px=A, pc=A, po=None, ps=A, tm=A, st=None, ws=WS,
+             wsb=lib.moe_workspace_size(50, 6, 64, 8))
+    a.update(kw)
+    st = lib.moe_dedup_dispatch(a["x"], a["xdt"], a["T"], a["H"], a["idx"], a["K"], a["E"], a["R"],
+                                a["rx"], a["rr"], a["rc"], a["ro"], a["rs"], a["rsl"], a["cap"],
+                                a["pr"], a["px"], a["pc"], a["po"], a["ps"], a["tm"], a["st"],
+                                a["ws"], a["wsb"], None)
+    return [st, lib.moe_last_error().decode()]
+
+res["dedup"] = {
+    "R0": dd(R=0), "R33": dd(R=33), "R_not_divisor": dd(R=7), "recv_null": dd(rx=None),
+    "rank_slot_null": dd(rsl=None), "ws_small": dd(wsb=100), "recv_rows_neg": dd(rr=-1),
+    "fp8": dd(xdt=2),
+}
+res["dequant"] = {
+    "H64": [lib.moe_fp8_dequant(A, A, 4, 64, A, None), lib.moe_last_error().decode()],
+    "rows_neg": [lib.moe_fp8_dequant(A, A, -1, 128, A, None), lib.moe_last_error().decode()],
+    "scales_null": [lib.moe_fp8_dequant(A, None, 4, 128, A, None), lib.moe_last_error().decode()],
+}
+res["route"] = {
+    "cnt_null": [lib.moe_route_count(A, 10, 2, 4, None, A, None, WS, 1 << 20, None),
+                 lib.moe_last_error().decode()],
+    "ws_small": [lib.moe_route_count(A, 10, 2, 4, A, A, None, WS, 0, None),
+                 lib.moe_last_error().decode()],
+}
+print(json.dumps(res))
+""")
+
+
+def _run_child():
+    env = dict(os.environ, ROCR_VISIBLE_DEVICES="-1", HIP_VISIBLE_DEVICES="-1")
+    code = f"ROOT = {ROOT!r}\nNAMES = {_declared_functions()!r}\n" + CHILD
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env,
+                       timeout=120)
+    assert r.returncode == 0, r.stderr
+    import json
+    return json.loads(r.stdout.strip().splitlines()[-1])
+
+
+_RES = None
+
+
+def _res():
+    global _RES
+    if _RES is None:
+        _RES = _run_child()
+    return _RES
+
+
+def test_library_exports_every_declared_function():
+    ex = _res()["exports"]
+    assert ex and all(ex.values()), ex
+
+
+def test_workspace_size():
+    ws = _res()["ws"]
+    assert ws[0] == ws[1] > 0          # deterministic
+    assert ws[2] > 0 and ws[3] > 0 and ws[4] > 0
+    assert ws[5] == 0                  # invalid sizes give 0
+    assert all(w % 256 == 0 for w in ws)
+    assert _res()["version"] >> 16 == 1
+
+
+INVALID, UNSUPPORTED, WORKSPACE = -1, -2, -3
+
+
+def test_dispatch_argument_errors():
+    d = _res()["dispatch"]
+    expect_ws = {"ws_small", "ws_null", "ws_unaligned"}
+    for case, (st, msg) in d.items():
+        if case in expect_ws:
+            assert st == WORKSPACE, (case, st, msg)
+        elif case == "fp8_from_f32":
+            assert st == UNSUPPORTED, (case, st, msg)
+        else:
+            assert st == INVALID, (case, st, msg)
+        assert msg, case
+
+
+def test_combine_argument_errors():
+    for case, (st, msg) in _res()["combine"].items():
+        assert st == (UNSUPPORTED if case == "y_fp8" else INVALID), (case, st, msg)
+        assert msg
+
+
+def test_dedup_and_helpers_argument_errors():
+    for case, (st, msg) in _res()["dedup"].items():
+        assert st == (WORKSPACE if case == "ws_small" else INVALID), (case, st, msg)
+    for case, (st, msg) in _res()["dequant"].items():
+        assert st == INVALID, (case, st, msg)
+    r = _res()["route"]
+    assert r["cnt_null"][0] == INVALID and r["ws_small"][0] == WORKSPACE
