@@ -40,11 +40,13 @@ class DedupPlan(ctypes.Structure):
 _lib = None
 
 
-def load(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load the library once; raises if it has not been built."""
+def load(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load the library once (MOE_ROUTE_LIB overrides the in-tree path);
+    raises if it has not been built."""
     global _lib
     if _lib is not None:
         return _lib
+    path = path or os.environ.get("MOE_ROUTE_LIB") or LIB_PATH
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with "
                            "`python -m combine_moe_route_count_amd.build`")

@@ -33,7 +33,7 @@ template <>
 struct Unit<false> {  // bf16: one 16-byte load
     u32x4 a;
     __device__ __forceinline__ void load(const void* y, int64_t row, int64_t H, int64_t col) {
-        a = ld16((const uint16_t*)y + row * H + col);
+        a = ld16_stream((const uint16_t*)y + row * H + col);
     }
     __device__ __forceinline__ float get(int j) const {
         return (j & 1) ? bf16hi(a[j >> 1]) : bf16lo(a[j >> 1]);
@@ -45,8 +45,8 @@ struct Unit<true> {  // f32: two 16-byte loads
     u32x4 a, b;
     __device__ __forceinline__ void load(const void* y, int64_t row, int64_t H, int64_t col) {
         const float* p = (const float*)y + row * H + col;
-        a = ld16(p);
-        b = ld16(p + 4);
+        a = ld16_stream(p);
+        b = ld16_stream(p + 4);
     }
     __device__ __forceinline__ float get(int j) const {
         return __builtin_bit_cast(float, j < 4 ? a[j] : b[j - 4]);
@@ -64,13 +64,13 @@ __device__ __forceinline__ void store_unit(void* out, int64_t row, int64_t H, in
             a[j] = __builtin_bit_cast(uint32_t, acc[j]);
             b[j] = __builtin_bit_cast(uint32_t, acc[4 + j]);
         }
-        st16(p, a);
-        st16(p + 4, b);
+        st16_stream(p, a);
+        st16_stream(p + 4, b);
     } else {
         u32x4 a;
 #pragma unroll
         for (int j = 0; j < 4; ++j) a[j] = pack_bf16x2(acc[2 * j], acc[2 * j + 1]);
-        st16((uint16_t*)out + row * H + col, a);
+        st16_stream((uint16_t*)out + row * H + col, a);
     }
 }
 

@@ -142,12 +142,45 @@ __global__ __launch_bounds__(kRankThreads) void rank_tiles_kernel(
 }
 
 constexpr int kScanThreads = 1024;
+constexpr int kScanCache = 16;  // tile counts a scan thread keeps in registers
 
+// Exclusive scan of one int per thread over the block (initial value 0).
+__device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t* wave_sums) {
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave;
+    const int wave = tid / kWave;
+    int32_t x = v;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int32_t y = __shfl_up(x, d, kWave);
+        if (lane >= d) x += y;
+    }
+    if (lane == kWave - 1) wave_sums[wave] = x;
+    __syncthreads();
+    if (wave == 0) {
+        int32_t ws = lane < kScanThreads / kWave ? wave_sums[lane] : 0;
+#pragma unroll
+        for (int d = 1; d < kScanThreads / kWave; d <<= 1) {
+            const int32_t y = __shfl_up(ws, d, kWave);
+            if (lane >= d) ws += y;
+        }
+        if (lane < kScanThreads / kWave) wave_sums[lane] = ws;  // inclusive wave totals
+    }
+    __syncthreads();
+    const int32_t before = wave > 0 ? wave_sums[wave - 1] : 0;
+    return before + x - v;
+}
+
+// One workgroup.  Thread (key, part) owns the tiles [t0, t1) of one key: it
+// loads their counts once (all loads issued together), sums them, takes the
+// prefix of the earlier parts from LDS and writes the exclusive tile bases.
+// The per-key totals are then scanned over keys for the offsets.
 __global__ __launch_bounds__(kScanThreads) void scan_tiles_kernel(ScanArgs a) {
     __shared__ int32_t part_sum[kScanThreads];
-    __shared__ int32_t buf[kScanThreads];
+    __shared__ int32_t key_total[kScanThreads];
+    __shared__ int32_t wave_sums[kScanThreads / kWave];
     __shared__ int32_t red[2];
-    __shared__ int64_t red_drop;
+    __shared__ unsigned long long red_drop;
     const int tid = threadIdx.x;
     const int NK = a.NK;
     const int tiles = a.tiles;
@@ -161,57 +194,56 @@ __global__ __launch_bounds__(kScanThreads) void scan_tiles_kernel(ScanArgs a) {
     const int t0 = part * tpp;
     const int t1 = (t0 + tpp < tiles) ? t0 + tpp : tiles;
 
+    int32_t c[kScanCache];
+    int32_t s = 0;
+#pragma unroll
+    for (int i = 0; i < kScanCache; ++i) {
+        const int tl = t0 + i;
+        c[i] = (active && tl < t1) ? a.tile_cnt[(int64_t)tl * NK + key] : 0;
+    }
+    int32_t fi = 0, fd = 0;
+    for (int tl = tid; tl < tiles; tl += kScanThreads) {
+        fi += a.tile_flags[2 * (int64_t)tl];
+        fd += a.tile_flags[2 * (int64_t)tl + 1];
+    }
+#pragma unroll
+    for (int i = 0; i < kScanCache; ++i) s += c[i];
+    if (active)
+        for (int tl = t0 + kScanCache; tl < t1; ++tl) s += a.tile_cnt[(int64_t)tl * NK + key];
     if (tid == 0) {
         red[0] = 0;
         red[1] = 0;
         red_drop = 0;
     }
-    // 1. per-part sums over its tile range
-    int32_t s = 0;
-    if (active)
-        for (int tl = t0; tl < t1; ++tl) s += a.tile_cnt[(int64_t)tl * NK + key];
     part_sum[tid] = s;
+    key_total[tid] = 0;
     __syncthreads();
 
-    // 2. rescan the range from the part's prefix: exclusive tile bases
-    int32_t total = 0;
+    if (fi) atomicAdd(&red[0], fi);
+    if (fd) atomicAdd(&red[1], fd);
     if (active) {
         int32_t run = 0;
         for (int p = 0; p < part; ++p) run += part_sum[p * NK + key];
-        for (int tl = t0; tl < t1; ++tl) {
-            const int64_t i = (int64_t)tl * NK + key;
-            const int32_t c = a.tile_cnt[i];
-            a.tile_cnt[i] = run;
-            run += c;
+#pragma unroll
+        for (int i = 0; i < kScanCache; ++i) {
+            const int tl = t0 + i;
+            if (tl < t1) a.tile_cnt[(int64_t)tl * NK + key] = run;
+            run += c[i];
         }
-        if (part == parts - 1) total = run;
-    }
-    // 3. flags: invalid ids and entries dropped before slotting
-    {
-        int32_t fi = 0, fd = 0;
-        for (int tl = tid; tl < tiles; tl += kScanThreads) {
-            fi += a.tile_flags[2 * (int64_t)tl];
-            fd += a.tile_flags[2 * (int64_t)tl + 1];
+        for (int tl = t0 + kScanCache; tl < t1; ++tl) {
+            const int64_t j = (int64_t)tl * NK + key;
+            const int32_t cc = a.tile_cnt[j];
+            a.tile_cnt[j] = run;
+            run += cc;
         }
-        __syncthreads();
-        if (fi) atomicAdd(&red[0], fi);
-        if (fd) atomicAdd(&red[1], fd);
+        if (part == parts - 1) key_total[key] = run;
     }
-    // 4. exclusive scan of the per-key totals (Hillis-Steele over the block)
-    if (active && part == parts - 1) buf[key] = total;
-    if (tid >= NK) buf[tid] = 0;
     __syncthreads();
-    const int32_t mine = buf[tid];
-    for (int d = 1; d < NK; d <<= 1) {
-        const int32_t add = tid >= d ? buf[tid - d] : 0;
-        __syncthreads();
-        buf[tid] += add;
-        __syncthreads();
-    }
-    const int32_t incl = buf[tid];
-    const int32_t excl = incl - mine;
 
-    // 5. offsets, segments under the capacity, dropped counts
+    const int32_t mine = key_total[tid];
+    const int32_t excl = block_exclusive_scan(mine, wave_sums);
+    const int32_t incl = excl + mine;
+
     if (tid < NK) {
         const int64_t cnt = mine;
         a.off_ws[tid] = excl;
@@ -231,7 +263,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_tiles_kernel(ScanArgs a) {
             const int64_t bend = a.cap > 0 ? (int64_t)NK * a.cap : (int64_t)incl;
             if (a.packed_off) a.packed_off[NK] = (int32_t)(bend < a.rows_limit ? bend : a.rows_limit);
         }
-        if (cnt - pc) atomicAdd((unsigned long long*)&red_drop, (unsigned long long)(cnt - pc));
+        if (cnt - pc) atomicAdd(&red_drop, (unsigned long long)(cnt - pc));
     }
     __syncthreads();
     if (tid == 0 && a.stats) {

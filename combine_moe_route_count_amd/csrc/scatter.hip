@@ -57,7 +57,7 @@ __device__ __forceinline__ void store_row_copies(const char* src, int nvec, char
 #pragma unroll
             for (int i = 0; i < VPT; ++i) {
                 const int v = base + tid + i * (int)blockDim.x;
-                if (v < nvec) st16(out + (int64_t)v * 16, val[i]);
+                if (v < nvec) st16_stream(out + (int64_t)v * 16, val[i]);
             }
         }
         base += step;
@@ -65,7 +65,7 @@ __device__ __forceinline__ void store_row_copies(const char* src, int nvec, char
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
             const int v = base + tid + i * (int)blockDim.x;
-            if (v < nvec) val[i] = ld16(src + (int64_t)v * 16);
+            if (v < nvec) val[i] = ld16_stream(src + (int64_t)v * 16);
         }
     }
 }
@@ -75,7 +75,7 @@ __device__ __forceinline__ void load_first_pass(const char* src, int nvec, u32x4
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
         const int v = threadIdx.x + i * (int)blockDim.x;
-        if (v < nvec) val[i] = ld16(src + (int64_t)v * 16);
+        if (v < nvec) val[i] = ld16_stream(src + (int64_t)v * 16);
     }
 }
 
@@ -167,8 +167,8 @@ __global__ __launch_bounds__(kCopyThreads) void scatter_fp8_kernel(ScatterArgs a
         for (int i = 0; i < UPT; ++i) {
             const int u = base + tid + i * (int)blockDim.x;
             if (u < nunits) {
-                lo[i] = ld16(src + (int64_t)u * 32);
-                hi[i] = ld16(src + (int64_t)u * 32 + 16);
+                lo[i] = ld16_stream(src + (int64_t)u * 32);
+                hi[i] = ld16_stream(src + (int64_t)u * 32 + 16);
             } else {
                 lo[i] = u32x4{0, 0, 0, 0};
                 hi[i] = u32x4{0, 0, 0, 0};
@@ -189,8 +189,8 @@ __global__ __launch_bounds__(kCopyThreads) void scatter_fp8_kernel(ScatterArgs a
             for (int i = 0; i < UPT; ++i) {
                 const int u = base + tid + i * (int)blockDim.x;
                 if (u < nunits) {
-                    st16(out + (int64_t)u * 16, q[i]);
-                    if ((u & 7) == 0) sc[u >> 3] = s[i];
+                    st16_stream(out + (int64_t)u * 16, q[i]);
+                    if ((u & 7) == 0) __builtin_nontemporal_store(s[i], sc + (u >> 3));
                 }
             }
         }
@@ -272,7 +272,7 @@ __global__ __launch_bounds__(kCopyThreads) void expand_kernel(ExpandArgs a) {
 #pragma unroll
             for (int i = 0; i < VPT; ++i) {
                 const int v = base + tid + i * (int)blockDim.x;
-                if (v < nvec) val[i] = ld16(src + (int64_t)v * 16);
+                if (v < nvec) val[i] = ld16_stream(src + (int64_t)v * 16);
             }
 #pragma unroll
             for (int k = 0; k < KMAX; ++k) {
