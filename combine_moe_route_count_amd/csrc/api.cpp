@@ -8,7 +8,7 @@
 #include <cstdio>
 #include <string>
 
-#include "../../include/moe_route.h"
+#include "moe_route.h"
 #include "internal.hpp"
 
 #define MOE_API extern "C" __attribute__((visibility("default")))

@@ -82,10 +82,12 @@ __device__ __forceinline__ void token_entries(const CombineArgs& a, int64_t t, i
     int my_row = -1;
     float my_w = 0.0f;
     if (lane < a.K) {
+        // both loads in flight together: one memory round trip before the gather
         const int64_t r = a.tok_map[t * a.K + lane];
+        const float wk = a.w[t * a.K + lane];
         if (r >= 0 && r < a.y_rows) {
             my_row = (int)r;
-            my_w = a.w[t * a.K + lane];
+            my_w = wk;
         }
     }
 #pragma unroll
@@ -284,10 +286,12 @@ int comb_threads(int units, int vpt) {
     return th;
 }
 
+// One unit per lane and pass: few VGPRs, so four 8-wave workgroups fit on a CU
+// and one workgroup's routing latency hides behind the others' gathers.
 template <bool YF32, bool OF32, int KMAX>
 void plain_go(const CombineArgs& a, hipStream_t s) {
     const int units = (int)(a.H / 8);
-    constexpr int VPT = YF32 ? 1 : 2;
+    constexpr int VPT = 1;
     combine_kernel<YF32, OF32, KMAX, VPT>
         <<<dim3((unsigned)a.T), dim3(comb_threads(units, VPT)), 0, s>>>(a);
 }

@@ -190,7 +190,7 @@ __global__ __launch_bounds__(kCopyThreads) void scatter_fp8_kernel(ScatterArgs a
                 const int u = base + tid + i * (int)blockDim.x;
                 if (u < nunits) {
                     st16_stream(out + (int64_t)u * 16, q[i]);
-                    if ((u & 7) == 0) __builtin_nontemporal_store(s[i], sc + (u >> 3));
+                    if ((u & 7) == 0) sc[u >> 3] = s[i];  // cached: L2 merges the 32-byte pieces of a scale row
                 }
             }
         }
