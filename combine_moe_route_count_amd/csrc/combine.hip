@@ -23,7 +23,7 @@ namespace moe {
 
 namespace {
 
-constexpr int kCombThreads = 512;
+constexpr int kCombThreads = 256;
 
 // 8 consecutive elements of row `row` starting at element col, as f32.
 template <bool YF32>
@@ -97,55 +97,73 @@ __device__ __forceinline__ void token_entries(const CombineArgs& a, int64_t t, i
     }
 }
 
+// Work decomposition: workgroup (c, t) owns units [c*C, c*C + C) of token t,
+// one 8-element unit per lane, so every lane issues the loads of all K rows at
+// once and there is no second pass.  Chunks of at most kChunkUnits units keep
+// the workgroups small enough that several fit on a CU and one workgroup's
+// routing round trip overlaps with the others' gathers.
+constexpr int kChunkUnits = 256;
+
+struct Chunking {
+    int units;   // 8-element units per row
+    int nch;     // chunks per token
+    int C;       // units per chunk
+};
+
+inline Chunking chunking(int64_t H) {
+    Chunking ch;
+    ch.units = (int)(H / 8);
+    ch.nch = (ch.units + kChunkUnits - 1) / kChunkUnits;
+    ch.C = (ch.units + ch.nch - 1) / ch.nch;
+    return ch;
+}
+
 // ---------------------------------------------------------------------------
 // plain combine: acc = 0; acc = acc + w_k * y_k for k ascending
 // ---------------------------------------------------------------------------
-template <bool YF32, bool OF32, int KMAX, int VPT>
-__global__ __launch_bounds__(kCombThreads) void combine_kernel(CombineArgs a) {
-    const int64_t t = blockIdx.x;
-    const int tid = threadIdx.x;
+template <bool YF32, bool OF32, int KMAX>
+__device__ __forceinline__ void combine_item(const CombineArgs& a, int64_t t, int c, int C) {
     const int64_t H = a.H;
     const int units = (int)(H / 8);
     int rows[KMAX];
     float w[KMAX];
     token_entries<KMAX>(a, t, rows, w);
 
-    for (int base = 0; base < units; base += VPT * (int)blockDim.x) {
-        Unit<YF32> y[KMAX][VPT];
+    const int u = c * C + (int)threadIdx.x;
+    if ((int)threadIdx.x < C && u < units) {
+        Unit<YF32> y[KMAX];
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k)
+            if (rows[k] >= 0) y[k].load(a.y, rows[k], H, (int64_t)u * 8);
+        float acc[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) {
             if (rows[k] < 0) continue;
 #pragma unroll
-            for (int i = 0; i < VPT; ++i) {
-                const int u = base + tid + i * (int)blockDim.x;
-                if (u < units) y[k][i].load(a.y, rows[k], H, (int64_t)u * 8);
+            for (int j = 0; j < 8; ++j) {
+                const float p = w[k] * y[k].get(j);
+                acc[j] = acc[j] + p;
             }
         }
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int u = base + tid + i * (int)blockDim.x;
-            if (u >= units) continue;
-            float acc[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
-#pragma unroll
-            for (int k = 0; k < KMAX; ++k) {
-                if (rows[k] < 0) continue;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const float p = w[k] * y[k][i].get(j);
-                    acc[j] = acc[j] + p;
-                }
-            }
-            store_unit<OF32>(a.out, t, H, (int64_t)u * 8, acc);
-        }
+        store_unit<OF32>(a.out, t, H, (int64_t)u * 8, acc);
     }
-    if (tid == 0 && a.out_weights) {
+    if (c == 0 && threadIdx.x == 0 && a.out_weights) {
         float s = 0.0f;
 #pragma unroll
         for (int k = 0; k < KMAX; ++k)
             if (rows[k] >= 0) s = s + w[k];
         a.out_weights[t] = s;
+    }
+}
+
+template <bool YF32, bool OF32, int KMAX>
+__global__ __launch_bounds__(kCombThreads) void combine_kernel(CombineArgs a, int C, int nch) {
+    const int64_t items = a.T * nch;
+    for (int64_t wi = blockIdx.x; wi < items; wi += gridDim.x) {
+        const int64_t t = wi / nch;
+        combine_item<YF32, OF32, KMAX>(a, t, (int)(wi - t * nch), C);
     }
 }
 
@@ -167,29 +185,46 @@ __device__ __forceinline__ void entry_ranks(const CombineArgs& a, int64_t t, int
     for (int k = 0; k < KMAX; ++k) ranks[k] = readlane(my_rank, k);
 }
 
+// Sum of the weights of the token's contributing entries, per rank then across
+// ranks in ascending order (the grouping of the dedup combine).
+template <int KMAX>
+__device__ __forceinline__ float dedup_weight_sum(const CombineArgs& a, int64_t t,
+                                                  const int (&rows)[KMAX], const int (&ranks)[KMAX],
+                                                  const float (&w)[KMAX]) {
+    float s = 0.0f;
+    for (int r = 0; r < a.R; ++r) {
+        const int32_t rs = a.rank_slot[t * a.R + r];
+        if (rs < 0 || rs >= a.recv_rows) continue;
+        float pw = 0.0f;
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k)
+            if (rows[k] >= 0 && ranks[k] == r) pw = pw + w[k];
+        s = s + pw;
+    }
+    return s;
+}
+
 template <bool YF32, bool OF32, int KMAX, int MODE>
-__global__ __launch_bounds__(kCombThreads) void dedup_combine_kernel(CombineArgs a) {
-    const int64_t t = blockIdx.x;
-    const int tid = threadIdx.x;
+__device__ __forceinline__ void dedup_item(const CombineArgs& a, int64_t t, int c, int C) {
     const int64_t H = a.H;
     const int units = (int)(H / 8);
-    const int R = a.R;
     int rows[KMAX], ranks[KMAX];
     float w[KMAX];
     token_entries<KMAX>(a, t, rows, w);
     entry_ranks<KMAX>(a, t, ranks);
 
-    for (int u = tid; u < units; u += (int)blockDim.x) {
+    const int u = c * C + (int)threadIdx.x;
+    if ((int)threadIdx.x < C && u < units) {
+        Unit<YF32> y[KMAX];
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k)
+            if (rows[k] >= 0) y[k].load(a.y, rows[k], H, (int64_t)u * 8);
         float acc[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
-        for (int r = 0; r < R; ++r) {
-            const int32_t rs = a.rank_slot[t * R + r];
+        for (int r = 0; r < a.R; ++r) {
+            const int32_t rs = a.rank_slot[t * a.R + r];
             if (rs < 0 || rs >= a.recv_rows) continue;
-            Unit<YF32> y[KMAX];
-#pragma unroll
-            for (int k = 0; k < KMAX; ++k)
-                if (rows[k] >= 0 && ranks[k] == r) y[k].load(a.y, rows[k], H, (int64_t)u * 8);
             float p[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) p[j] = 0.0f;
@@ -211,35 +246,31 @@ __global__ __launch_bounds__(kCombThreads) void dedup_combine_kernel(CombineArgs
         }
         if (MODE == 0) store_unit<OF32>(a.out, t, H, (int64_t)u * 8, acc);
     }
-    if (MODE == 0 && tid == 0 && a.out_weights) {
-        float s = 0.0f;
-        for (int r = 0; r < R; ++r) {
-            const int32_t rs = a.rank_slot[t * R + r];
-            if (rs < 0 || rs >= a.recv_rows) continue;
-            float pw = 0.0f;
-#pragma unroll
-            for (int k = 0; k < KMAX; ++k)
-                if (rows[k] >= 0 && ranks[k] == r) pw = pw + w[k];
-            s = s + pw;
-        }
-        a.out_weights[t] = s;
+    if (MODE == 0 && c == 0 && threadIdx.x == 0 && a.out_weights)
+        a.out_weights[t] = dedup_weight_sum<KMAX>(a, t, rows, ranks, w);
+}
+
+template <bool YF32, bool OF32, int KMAX, int MODE>
+__global__ __launch_bounds__(kCombThreads) void dedup_combine_kernel(CombineArgs a, int C, int nch) {
+    const int64_t items = a.T * nch;
+    for (int64_t wi = blockIdx.x; wi < items; wi += gridDim.x) {
+        const int64_t t = wi / nch;
+        dedup_item<YF32, OF32, KMAX, MODE>(a, t, (int)(wi - t * nch), C);
     }
 }
 
 // stage B: out[t] = 0 + partial[rank_slot[t][r]] for r ascending
 template <bool OF32, int KMAX>
-__global__ __launch_bounds__(kCombThreads) void dedup_sum_kernel(CombineArgs a) {
-    const int64_t t = blockIdx.x;
-    const int tid = threadIdx.x;
+__device__ __forceinline__ void dedup_sum_item(const CombineArgs& a, int64_t t, int c, int C) {
     const int64_t H = a.H;
     const int units = (int)(H / 8);
-    const int R = a.R;
-    for (int u = tid; u < units; u += (int)blockDim.x) {
+    const int u = c * C + (int)threadIdx.x;
+    if ((int)threadIdx.x < C && u < units) {
         float acc[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
-        for (int r = 0; r < R; ++r) {
-            const int32_t rs = a.rank_slot[t * R + r];
+        for (int r = 0; r < a.R; ++r) {
+            const int32_t rs = a.rank_slot[t * a.R + r];
             if (rs < 0 || rs >= a.recv_rows) continue;
             Unit<true> p;
             p.load(a.partial, rs, H, (int64_t)u * 8);
@@ -248,63 +279,49 @@ __global__ __launch_bounds__(kCombThreads) void dedup_sum_kernel(CombineArgs a) 
         }
         store_unit<OF32>(a.out, t, H, (int64_t)u * 8, acc);
     }
-    if (tid == 0 && a.out_weights) {
+    if (c == 0 && a.out_weights) {
         int rows[KMAX], ranks[KMAX];
         float w[KMAX];
-        // entries are read by lane 0 alone here: no wave-wide broadcast needed
-        for (int k = 0; k < KMAX; ++k) {
-            rows[k] = -1;
-            ranks[k] = -1;
-            w[k] = 0.0f;
-            if (k >= a.K) continue;
-            const int64_t r = a.tok_map[t * a.K + k];
-            const int32_t e = a.idx[t * a.K + k];
-            if (r >= 0 && r < a.y_rows && e >= 0 && e < a.E) {
-                rows[k] = (int)r;
-                ranks[k] = e / (a.E / a.R);
-                w[k] = a.w[t * a.K + k];
-            }
-        }
-        float s = 0.0f;
-        for (int r = 0; r < R; ++r) {
-            const int32_t rs = a.rank_slot[t * R + r];
-            if (rs < 0 || rs >= a.recv_rows) continue;
-            float pw = 0.0f;
-            for (int k = 0; k < KMAX; ++k)
-                if (rows[k] >= 0 && ranks[k] == r) pw = pw + w[k];
-            s = s + pw;
-        }
-        a.out_weights[t] = s;
+        token_entries<KMAX>(a, t, rows, w);
+        entry_ranks<KMAX>(a, t, ranks);
+        if (threadIdx.x == 0) a.out_weights[t] = dedup_weight_sum<KMAX>(a, t, rows, ranks, w);
     }
 }
 
-int comb_threads(int units, int vpt) {
-    int per = (units + vpt - 1) / vpt;
-    int th = ((per + kWave - 1) / kWave) * kWave;
-    if (th > kCombThreads) th = kCombThreads;
-    if (th < kWave) th = kWave;
-    return th;
+template <bool OF32, int KMAX>
+__global__ __launch_bounds__(kCombThreads) void dedup_sum_kernel(CombineArgs a, int C, int nch) {
+    const int64_t items = a.T * nch;
+    for (int64_t wi = blockIdx.x; wi < items; wi += gridDim.x) {
+        const int64_t t = wi / nch;
+        dedup_sum_item<OF32, KMAX>(a, t, (int)(wi - t * nch), C);
+    }
 }
 
-// One unit per lane and pass: few VGPRs, so four 8-wave workgroups fit on a CU
-// and one workgroup's routing latency hides behind the others' gathers.
+int threads_for(int C) {
+    int th = ((C + kWave - 1) / kWave) * kWave;
+    return th < kWave ? kWave : th;
+}
+
+dim3 item_grid(int64_t items) {
+    return dim3((unsigned)(items < kMaxGrid ? items : kMaxGrid));
+}
+
 template <bool YF32, bool OF32, int KMAX>
 void plain_go(const CombineArgs& a, hipStream_t s) {
-    const int units = (int)(a.H / 8);
-    constexpr int VPT = 1;
-    combine_kernel<YF32, OF32, KMAX, VPT>
-        <<<dim3((unsigned)a.T), dim3(comb_threads(units, VPT)), 0, s>>>(a);
+    const Chunking ch = chunking(a.H);
+    combine_kernel<YF32, OF32, KMAX>
+        <<<item_grid(a.T * ch.nch), dim3(threads_for(ch.C)), 0, s>>>(a, ch.C, ch.nch);
 }
 
 template <bool YF32, bool OF32, int KMAX>
 void dedup_go(const CombineArgs& a, hipStream_t s) {
-    const int units = (int)(a.H / 8);
-    const dim3 grid((unsigned)a.T), block(comb_threads(units, 1));
+    const Chunking ch = chunking(a.H);
+    const dim3 grid = item_grid(a.T * ch.nch), block(threads_for(ch.C));
     if (a.partial) {
-        dedup_combine_kernel<YF32, OF32, KMAX, 1><<<grid, block, 0, s>>>(a);
-        dedup_sum_kernel<OF32, KMAX><<<grid, block, 0, s>>>(a);
+        dedup_combine_kernel<YF32, OF32, KMAX, 1><<<grid, block, 0, s>>>(a, ch.C, ch.nch);
+        dedup_sum_kernel<OF32, KMAX><<<grid, block, 0, s>>>(a, ch.C, ch.nch);
     } else {
-        dedup_combine_kernel<YF32, OF32, KMAX, 0><<<grid, block, 0, s>>>(a);
+        dedup_combine_kernel<YF32, OF32, KMAX, 0><<<grid, block, 0, s>>>(a, ch.C, ch.nch);
     }
 }
 

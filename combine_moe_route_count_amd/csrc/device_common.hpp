@@ -16,6 +16,10 @@ constexpr int kTileChunks = 4;
 constexpr int kTile = kTileWaves * kTileChunks * kWave;
 constexpr int kRankThreads = kTileWaves * kWave;
 
+// Token-parallel kernels launch at most this many workgroups and loop over the
+// rest, which keeps every launch far below the 2^32 work-item limit.
+constexpr int64_t kMaxGrid = (int64_t)1 << 22;
+
 constexpr int kFp8Block = 128;
 constexpr float kE4m3Max = 448.0f;
 

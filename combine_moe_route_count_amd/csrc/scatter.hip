@@ -83,8 +83,7 @@ __device__ __forceinline__ void load_first_pass(const char* src, int nvec, u32x4
 // plain dispatch, bit copy (bf16 or f32)
 // ---------------------------------------------------------------------------
 template <int DMAX, int VPT>
-__global__ __launch_bounds__(kCopyThreads) void scatter_copy_kernel(ScatterArgs a) {
-    const int64_t t = blockIdx.x;
+__device__ __forceinline__ void scatter_copy_kernel_item(const ScatterArgs& a, int64_t t) {
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
     const int K = a.slot.K;
@@ -144,8 +143,7 @@ __device__ __forceinline__ void fp8_pack16(const u32x4& lo, const u32x4& hi, u32
 }
 
 template <int DMAX, int UPT>
-__global__ __launch_bounds__(kCopyThreads) void scatter_fp8_kernel(ScatterArgs a) {
-    const int64_t t = blockIdx.x;
+__device__ __forceinline__ void scatter_fp8_kernel_item(const ScatterArgs& a, int64_t t) {
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
     const int K = a.slot.K;
@@ -201,8 +199,7 @@ __global__ __launch_bounds__(kCopyThreads) void scatter_fp8_kernel(ScatterArgs a
 // dedup stage 1: one copy of x[t] per (t, r) in the token's rank mask
 // ---------------------------------------------------------------------------
 template <int DMAX, int VPT>
-__global__ __launch_bounds__(kCopyThreads) void recv_copy_kernel(RecvArgs a) {
-    const int64_t t = blockIdx.x;
+__device__ __forceinline__ void recv_copy_kernel_item(const RecvArgs& a, int64_t t) {
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
     const int R = a.R;
@@ -236,8 +233,7 @@ __global__ __launch_bounds__(kCopyThreads) void recv_copy_kernel(RecvArgs a) {
 // that rank (the same slots a plain dispatch of the surviving ids gives)
 // ---------------------------------------------------------------------------
 template <int KMAX, int VPT>
-__global__ __launch_bounds__(kCopyThreads) void expand_kernel(ExpandArgs a) {
-    const int64_t t = blockIdx.x;
+__device__ __forceinline__ void expand_kernel_item(const ExpandArgs& a, int64_t t) {
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
     const int K = a.slot.K;
@@ -287,6 +283,26 @@ __global__ __launch_bounds__(kCopyThreads) void expand_kernel(ExpandArgs a) {
             }
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// kernels: one source token per workgroup, grid-stride over tokens
+// ---------------------------------------------------------------------------
+template <int DMAX, int VPT>
+__global__ __launch_bounds__(kCopyThreads) void scatter_copy_kernel(ScatterArgs a) {
+    for (int64_t t = blockIdx.x; t < a.T; t += gridDim.x) scatter_copy_kernel_item<DMAX, VPT>(a, t);
+}
+template <int DMAX, int UPT>
+__global__ __launch_bounds__(kCopyThreads) void scatter_fp8_kernel(ScatterArgs a) {
+    for (int64_t t = blockIdx.x; t < a.T; t += gridDim.x) scatter_fp8_kernel_item<DMAX, UPT>(a, t);
+}
+template <int DMAX, int VPT>
+__global__ __launch_bounds__(kCopyThreads) void recv_copy_kernel(RecvArgs a) {
+    for (int64_t t = blockIdx.x; t < a.T; t += gridDim.x) recv_copy_kernel_item<DMAX, VPT>(a, t);
+}
+template <int KMAX, int VPT>
+__global__ __launch_bounds__(kCopyThreads) void expand_kernel(ExpandArgs a) {
+    for (int64_t t = blockIdx.x; t < a.T; t += gridDim.x) expand_kernel_item<KMAX, VPT>(a, t);
 }
 
 // ---------------------------------------------------------------------------
@@ -373,7 +389,7 @@ struct LaunchExpand {
 
 hipError_t launch_scatter(const ScatterArgs& a, hipStream_t s) {
     if (a.T == 0) return hipSuccess;
-    const dim3 grid((unsigned)a.T);
+    const dim3 grid((unsigned)(a.T < kMaxGrid ? a.T : kMaxGrid));
     if (a.fp8) {
         const int nunits = (int)(a.H / 16);
         const int th = copy_threads<2>(nunits);
@@ -387,13 +403,15 @@ hipError_t launch_scatter(const ScatterArgs& a, hipStream_t s) {
 hipError_t launch_recv_copy(const RecvArgs& a, hipStream_t s) {
     if (a.T == 0) return hipSuccess;
     const int nvec = (int)(a.H * a.x_bytes / 16);
-    return by_dmax<LaunchRecv, 4>(a.R, dim3((unsigned)a.T), copy_threads<4>(nvec), a, s);
+    const dim3 grid((unsigned)(a.T < kMaxGrid ? a.T : kMaxGrid));
+    return by_dmax<LaunchRecv, 4>(a.R, grid, copy_threads<4>(nvec), a, s);
 }
 
 hipError_t launch_expand(const ExpandArgs& a, hipStream_t s) {
     if (a.T == 0) return hipSuccess;
     const int nvec = (int)(a.H * a.x_bytes / 16);
-    return by_dmax<LaunchExpand, 4>(a.slot.K, dim3((unsigned)a.T), copy_threads<4>(nvec), a, s);
+    const dim3 grid((unsigned)(a.T < kMaxGrid ? a.T : kMaxGrid));
+    return by_dmax<LaunchExpand, 4>(a.slot.K, grid, copy_threads<4>(nvec), a, s);
 }
 
 hipError_t launch_fp8_dequant(const uint8_t* q, const float* scales, int64_t rows, int64_t H,

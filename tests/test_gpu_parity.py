@@ -364,3 +364,26 @@ def test_repeat_launches_bitwise_identical():
         assert torch.equal(o2.tok_map, tm0) and torch.equal(o2.packed, pk0)
         assert torch.equal(o2.scales.view(torch.int32), sc0.view(torch.int32))
         assert torch.equal(out.view(torch.int16), out0.view(torch.int16))
+
+
+def test_grid_stride_wrap_past_max_grid():
+    """More tokens than the launch cap of 2^22 workgroups, so the token loops
+    wrap; small rows keep it cheap.  Covers dispatch, fp8 pack and combine."""
+    T, K, E, H = (1 << 22) + 37, 1, 4, 128
+    rng = np.random.default_rng(21)
+    idx = rng.integers(-1, E, size=(T, K)).astype(np.int32)
+    x = rng.integers(0, 1 << 16, size=(T, H), dtype=np.uint16)
+    x[(x & 0x7F80) == 0x7F80] = 0x3F80            # no inf/nan patterns
+    note(f"grid wrap T={T}")
+    for fp8 in (False, True):
+        o = gpu_dispatch(dev_bf16(x), idx, E, fp8=fp8)
+        ref = oracle.dispatch(x, "bf16", idx, E, packed_dt="fp8" if fp8 else None)
+        assert_dispatch_equal(o, ref, fp8=fp8)
+    w = rng.random((T, K)).astype(np.float32)
+    plain = oracle.dispatch(x, "bf16", idx, E)
+    out, ow = moe.combine(dev_bf16(plain["packed"]), dev(plain["tok_map"]), dev(w),
+                          out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    eo, ew = oracle.combine(plain["packed"], "bf16", plain["tok_map"], w, "f32")
+    _check_combine(host(out), eo, "f32")
+    np.testing.assert_array_equal(host(ow), ew)
