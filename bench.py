@@ -77,6 +77,56 @@ def stored_traffic(kernel_hash):
     return d.get("traffic_bytes_per_launch")
 
 
+COPY_BYTES = 1 << 30   # calibration copy: 1 GiB read + 1 GiB written per launch
+
+
+def calibrate_copy(steps):
+    """A plain device-to-device copy of known size, profiled with the same
+    counters as the kernels so their KiB readings can be scaled to bytes."""
+    import torch
+    a = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda:0")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"[bench] calibration copy of {COPY_BYTES} bytes x {steps} done")
+
+
+def _pmc_rows(path, kernel_substr):
+    import csv
+    vals = []
+    for r in csv.DictReader(open(path)):
+        if kernel_substr in r["Kernel_Name"]:
+            vals.append(float(r["Counter_Value"]))
+    return vals
+
+
+def pmc_summary(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, out_json):
+    """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the combine kernel,
+    scaled by what the same counters read for the 1 GiB calibration copy."""
+    f = _pmc_rows(fetch_csv, "combine_kernel")
+    wv = _pmc_rows(write_csv, "combine_kernel")
+    cf = _pmc_rows(cal_fetch_csv, "copy")
+    cw = _pmc_rows(cal_write_csv, "copy")
+    cf_avg = statistics.mean(x for x in cf if x > 0)
+    cw_avg = statistics.mean(x for x in cw if x > 0)
+    fetch_scale = COPY_BYTES / cf_avg     # bytes per counter unit
+    write_scale = COPY_BYTES / cw_avg
+    f_avg, w_avg = statistics.mean(f), statistics.mean(wv)
+    d = {"kernel": "combine_kernel", "workload": "skewed_fp8 T=8192 H=7168 E=256 K=8",
+         "fetch_size_avg": f_avg, "write_size_avg": w_avg, "dispatches": [len(f), len(wv)],
+         "calibration_copy_bytes": COPY_BYTES, "calibration_fetch_size": cf_avg,
+         "calibration_write_size": cw_avg, "fetch_bytes_per_unit": fetch_scale,
+         "write_bytes_per_unit": write_scale,
+         "fetch_bytes_per_launch": f_avg * fetch_scale, "write_bytes_per_launch": w_avg * write_scale,
+         "traffic_bytes_per_launch": f_avg * fetch_scale + w_avg * write_scale,
+         "combine_source_hash": source_hash(COMBINE_SOURCES)}
+    with open(out_json, "w") as fh:
+        json.dump(d, fh, indent=1)
+    print(json.dumps(d, indent=1))
+
+
 def cpu_baseline(name, T_full, sample_T):
     """The oracle, as it stands, on a bounded sample of the same workload."""
     import numpy as np
@@ -114,7 +164,15 @@ def main():
     ap.add_argument("--workload", default="skewed_fp8")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-sample", type=int, default=1024)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run the plain 1 GiB copy used to scale HBM counters")
+    ap.add_argument("--pmc-summary", nargs=5, metavar=("FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE", "OUT"),
+                    help="summarize rocprofv3 FETCH_SIZE / WRITE_SIZE csvs into OUT (json)")
     args = ap.parse_args()
+
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary)
+        return
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
@@ -130,6 +188,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        calibrate_copy(args.steps)
+        return
     name = args.workload
     d = W.make_inputs(name)
     T, H, E, K = d["T"], d["H"], d["E"], d["K"]
@@ -154,25 +215,27 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
-    n_ev = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_ev)]
 
     def step(i, events=None):
         st = sets[i % len(sets)]
-        if events:
+        if events is not None:
             events[0].record(stream)
         moe.dispatch(st["x"], idx, E, fp8=fp8, out=st["o"], ws=ws)
-        if events:
+        if events is not None and len(events) == 3:
             events[1].record(stream)
         moe.combine(st["y"], st["o"].tok_map, w, out=st["out"], out_weights=st["ow"])
-        if events:
-            events[2].record(stream)
+        if events is not None:
+            events[-1].record(stream)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} done")
 
+    # pass 1 (the headline): HIP events on the launch stream around each
+    # dispatch+combine pair, none between the two calls
+    n_ev = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_ev)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -180,14 +243,20 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     log(f"[bench] timed {args.steps} steps done")
+    pair_us = [ev[i][0].elapsed_time(ev[i][1]) * 1e3 for i in range(n_ev)]
+    wall_ms = (t1 - t0) * 1e3 / args.steps
 
-    disp_us = [ev[i][0].elapsed_time(ev[i][1]) * 1e3 for i in range(n_ev)]
-    comb_us = [ev[i][1].elapsed_time(ev[i][2]) * 1e3 for i in range(n_ev)]
-    tot_us = [a + b for a, b in zip(disp_us, comb_us)]
+    # pass 2 (breakdown): a marker between dispatch and combine as well
+    evb = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_ev)]
+    for i in range(args.steps):
+        step(i, evb[i])
+    torch.cuda.synchronize()
+    disp_us = [evb[i][0].elapsed_time(evb[i][1]) * 1e3 for i in range(n_ev)]
+    comb_us = [evb[i][1].elapsed_time(evb[i][2]) * 1e3 for i in range(n_ev)]
+
     # drop the first timed round (start transient), report the median
     med = lambda v: statistics.median(v[1:] if len(v) > 2 else v)
-    d_us, c_us, t_us = med(disp_us), med(comb_us), med(tot_us)
-    wall_ms = (t1 - t0) * 1e3 / args.steps
+    d_us, c_us, t_us = med(disp_us), med(comb_us), med(pair_us)
 
     # correctness spot check of the last step (identity expert telescopes)
     st = sets[(args.steps - 1) % len(sets)]
@@ -234,6 +303,8 @@ def main():
                    "buffer_sets": args.sets},
         "achieved_gbps": round(gbs, 1),
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "pair_us_min": round(min(pair_us[1:] if n_ev > 2 else pair_us), 2),
+        "pair_us_std": round(statistics.pstdev(pair_us[1:] if n_ev > 2 else pair_us), 2),
         "dispatch_us": round(d_us, 2),
         "combine_us": round(c_us, 2),
         "dispatch_gbps": round(disp_gbs, 1),
