@@ -3,6 +3,8 @@
 // first launch, so a call that returns an error has enqueued nothing.
 #include <hip/hip_runtime_api.h>
 
+#include <atomic>
+#include <chrono>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -69,12 +71,14 @@ RouteWs carve_route(Carve& c, int64_t N, int NK) {
 
 struct Layout {
     RouteWs experts, ranks;
+    size_t ticket;  // uint64_t arrival ticket of the one-launch routing
     size_t total;
 };
 
 Layout layout(int64_t T, int K, int E, int R) {
     Carve c;
     Layout L;
+    L.ticket = c.take(sizeof(uint64_t));
     L.experts = carve_route(c, T * K, E);
     if (R > 0) L.ranks = carve_route(c, T * R, R);
     L.total = c.total;
@@ -144,27 +148,28 @@ struct LevelOut {
     int32_t* stats = nullptr;
 };
 
-hipError_t route_level(void* ws, const RouteWs& L, moe::KeyKind kind, const int32_t* idx,
-                       const int32_t* rank_slot, int64_t N, int K, int E, int R, int NK,
-                       int64_t cap, int64_t rows_limit, const LevelOut& o, moe::StatsMode mode,
-                       hipStream_t s) {
-    moe::RankArgs ra;
-    ra.kind = kind;
-    ra.idx = idx;
-    ra.rank_slot = rank_slot;
-    ra.N = N;
-    ra.K = K;
-    ra.E = E;
-    ra.R = R;
-    ra.NK = NK;
-    ra.local_rank = at<int32_t>(ws, L.local_rank);
-    ra.tile_cnt = at<int32_t>(ws, L.tile_cnt);
-    ra.tile_flags = at<int32_t>(ws, L.tile_flags);
-    hipError_t e = moe::launch_rank(ra, s);
-    if (e != hipSuccess) return e;
+// A distinct nonzero tag per one-launch routing call, seeded from the clock so
+// a ticket left in a reused workspace by an earlier process cannot match.
+uint32_t next_epoch() {
+    static std::atomic<uint32_t> counter{(uint32_t)std::chrono::steady_clock::now()
+                                             .time_since_epoch()
+                                             .count() |
+                                         1u};
+    // A tag of four equal bytes could match a workspace filled by a byte memset.
+    uint32_t e;
+    do {
+        e = counter.fetch_add(1, std::memory_order_relaxed);
+    } while (e == (e & 0xFFu) * 0x01010101u);
+    return e;
+}
+
+hipError_t route_level(void* ws, const RouteWs& L, size_t ticket, moe::KeyKind kind,
+                       const int32_t* idx, const int32_t* rank_slot, int64_t N, int K, int E,
+                       int R, int NK, int64_t cap, int64_t rows_limit, const LevelOut& o,
+                       moe::StatsMode mode, hipStream_t s) {
     moe::ScanArgs sa;
-    sa.tile_cnt = ra.tile_cnt;
-    sa.tile_flags = ra.tile_flags;
+    sa.tile_cnt = at<int32_t>(ws, L.tile_cnt);
+    sa.tile_flags = at<int32_t>(ws, L.tile_flags);
     sa.tiles = (int)L.tiles;
     sa.NK = NK;
     sa.cap = cap;
@@ -176,6 +181,38 @@ hipError_t route_level(void* ws, const RouteWs& L, moe::KeyKind kind, const int3
     sa.packed_off = o.packed_off;
     sa.stats = o.stats;
     sa.mode = mode;
+    int nbits = 0;
+    while ((1 << nbits) < NK) ++nbits;
+    if (L.tiles > 0 && NK <= moe::kFusedMaxKeys) {
+        moe::RouteFusedArgs fa;
+        fa.kind = kind;
+        fa.idx = idx;
+        fa.rank_slot = rank_slot;
+        fa.N = N;
+        fa.K = K;
+        fa.E = E;
+        fa.R = R;
+        fa.nbits = nbits;
+        fa.local_rank = at<int32_t>(ws, L.local_rank);
+        fa.scan = sa;
+        fa.ticket = at<uint64_t>(ws, ticket);
+        fa.epoch = next_epoch();
+        return moe::launch_route_fused(fa, s);
+    }
+    moe::RankArgs ra;
+    ra.kind = kind;
+    ra.idx = idx;
+    ra.rank_slot = rank_slot;
+    ra.N = N;
+    ra.K = K;
+    ra.E = E;
+    ra.R = R;
+    ra.NK = NK;
+    ra.local_rank = at<int32_t>(ws, L.local_rank);
+    ra.tile_cnt = sa.tile_cnt;
+    ra.tile_flags = (int32_t*)sa.tile_flags;
+    hipError_t e = moe::launch_rank(ra, s);
+    if (e != hipSuccess) return e;
     return moe::launch_scan(sa, s);
 }
 
@@ -215,7 +252,7 @@ MOE_API int moe_route_count(const int32_t* idx, int64_t T, int K, int E, int32_t
     o.cnt_out = cnt;
     o.off_out = off;
     o.stats = stats;
-    MOE_HIP(route_level(ws, L.experts, moe::KeyKind::Experts, idx, nullptr, T * K, K, E, 0, E, 0,
+    MOE_HIP(route_level(ws, L.experts, L.ticket, moe::KeyKind::Experts, idx, nullptr, T * K, K, E, 0, E, 0,
                         INT64_MAX, o, moe::StatsMode::Plain, (hipStream_t)stream),
             "moe_route_count");
     return ok();
@@ -254,13 +291,6 @@ MOE_API int moe_dispatch(const void* x, moe_dtype x_dt, int64_t T, int64_t H, co
     MOE_TRY(check_ws(ws, ws_bytes, L.total));
     hipStream_t s = (hipStream_t)stream;
 
-    LevelOut o;
-    o.packed_cnt = packed_cnt;
-    o.packed_off = packed_off;
-    o.stats = stats;
-    MOE_HIP(route_level(ws, L.experts, moe::KeyKind::Experts, idx, nullptr, T * K, K, E, 0, E, cap,
-                        packed_rows, o, moe::StatsMode::Plain, s),
-            "moe_dispatch routing");
     moe::ScatterArgs sa;
     sa.slot = slot_args(ws, L.experts, idx, K, E, cap, packed_rows);
     sa.x = x;
@@ -272,6 +302,14 @@ MOE_API int moe_dispatch(const void* x, moe_dtype x_dt, int64_t T, int64_t H, co
     sa.scales = packed_scales;
     sa.packed_src = packed_src;
     sa.tok_map = tok_map;
+
+    LevelOut o;
+    o.packed_cnt = packed_cnt;
+    o.packed_off = packed_off;
+    o.stats = stats;
+    MOE_HIP(route_level(ws, L.experts, L.ticket, moe::KeyKind::Experts, idx, nullptr, T * K, K, E, 0, E, cap,
+                        packed_rows, o, moe::StatsMode::Plain, s),
+            "moe_dispatch routing");
     MOE_HIP(moe::launch_scatter(sa, s), "moe_dispatch scatter");
     return ok();
 }
@@ -369,7 +407,7 @@ MOE_API int moe_dedup_dispatch(const void* x, moe_dtype x_dt, int64_t T, int64_t
     ro.cnt_out = recv_cnt;
     ro.off_out = recv_off;
     ro.stats = stats;
-    MOE_HIP(route_level(ws, L.ranks, moe::KeyKind::Ranks, idx, nullptr, T * R, K, E, R, R, 0,
+    MOE_HIP(route_level(ws, L.ranks, L.ticket, moe::KeyKind::Ranks, idx, nullptr, T * R, K, E, R, R, 0,
                         recv_rows, ro, moe::StatsMode::RecvRows, s),
             "moe_dedup_dispatch rank routing");
     moe::RecvArgs rc;
@@ -392,7 +430,7 @@ MOE_API int moe_dedup_dispatch(const void* x, moe_dtype x_dt, int64_t T, int64_t
     eo.packed_cnt = packed_cnt;
     eo.packed_off = packed_off;
     eo.stats = stats;
-    MOE_HIP(route_level(ws, L.experts, moe::KeyKind::Survivors, idx, rank_slot, T * K, K, E, R, E,
+    MOE_HIP(route_level(ws, L.experts, L.ticket, moe::KeyKind::Survivors, idx, rank_slot, T * K, K, E, R, E,
                         cap, packed_rows, eo, moe::StatsMode::Experts, s),
             "moe_dedup_dispatch expert routing");
     moe::ExpandArgs ea;

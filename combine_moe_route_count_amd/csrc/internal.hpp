@@ -103,6 +103,28 @@ struct ExpandArgs {           // dedup stage 2: recv rows -> per-expert rows
 };
 hipError_t launch_expand(const ExpandArgs& a, hipStream_t s);
 
+// ---------------------------------------------------------------------------
+// routing in one launch: ranks, then the scan by the last routing workgroup
+// ---------------------------------------------------------------------------
+
+// Key counts up to which the one-launch routing is used: its rank pass keeps
+// 16 waves x NK running counts in LDS.
+constexpr int kFusedMaxKeys = 512;
+
+struct RouteFusedArgs {
+    KeyKind kind;
+    const int32_t* idx;
+    const int32_t* rank_slot;  // Survivors only
+    int64_t N;          // entries
+    int K, E, R;
+    int nbits;          // key bits of NK
+    int32_t* local_rank;
+    ScanArgs scan;      // tiles, NK, tile counts in the workspace, outputs
+    uint64_t* ticket;   // in the workspace: (epoch << 32) | tiles finished
+    uint32_t epoch;     // distinct per call, never 0
+};
+hipError_t launch_route_fused(const RouteFusedArgs& a, hipStream_t s);
+
 hipError_t launch_fp8_dequant(const uint8_t* q, const float* scales, int64_t rows, int64_t H,
                               void* y, hipStream_t s);
 

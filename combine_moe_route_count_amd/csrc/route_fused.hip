@@ -1,0 +1,95 @@
+// route_fused.hip - one routing level in one launch: stable per-tile ranks,
+// then the tile / key scan run by whichever routing workgroup finishes last.
+//
+// Workgroups of 1024 threads each rank one tile of 1024 entries (16 waves x one
+// 64-entry chunk, the pass of route.hip), write back their counts, and take a
+// ticket.  The workgroup that takes the last ticket runs the scan of
+// route.hip on everyone's counts and clears the ticket.  Nobody waits for
+// anybody: a workgroup either finishes after its tile or, being last, after the
+// scan, so the launch needs no co-residency and cannot hang (the CTA-local rule
+// of "Drop cooperative launch from the CTA-independent local kernels", MoonEP
+// pull 34, "Why it's worth doing").  Compared with two launches this saves one
+// kernel boundary on every routing level.
+#include "device_common.hpp"
+#include "internal.hpp"
+#include "route_device.hpp"
+
+namespace moe {
+
+namespace {
+
+constexpr int kFusedThreads = 1024;
+constexpr int kFusedWaves = kFusedThreads / kWave;
+
+// Arrival on the epoch-tagged ticket; returns this launch's count after the
+// arrival.  A stored epoch that differs (an earlier launch, a cleared ticket,
+// or whatever an uninitialised workspace holds) is replaced by (epoch, 1) with
+// one compare-and-swap; once the word carries this launch's epoch, arrivals
+// are plain fetch-adds, which the atomic unit serves back to back instead of
+// failing and retrying under contention.  The epoch cannot change under an
+// arrival: only the last arrival of this launch clears the word.
+__device__ uint32_t arrive_ticket(uint64_t* ticket, uint32_t epoch) {
+    uint64_t cur = __hip_atomic_load(ticket, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((uint32_t)(cur >> 32) != epoch) {
+        const uint64_t fresh = ((uint64_t)epoch << 32) | 1ull;
+        if (__hip_atomic_compare_exchange_strong(ticket, &cur, fresh, __ATOMIC_RELAXED,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+            return 1u;
+        // cur now holds the word that beat us; it is either this launch's
+        // (an arrival got there first) or still stale, in which case retry.
+        while ((uint32_t)(cur >> 32) != epoch) {
+            if (__hip_atomic_compare_exchange_strong(ticket, &cur, fresh, __ATOMIC_RELAXED,
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+                return 1u;
+        }
+    }
+    const uint64_t old =
+        __hip_atomic_fetch_add(ticket, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return (uint32_t)old + 1u;
+}
+
+template <class KeyFn>
+__global__ __launch_bounds__(kFusedThreads) void route_fused_kernel(KeyFn keys, RouteFusedArgs a) {
+    extern __shared__ int32_t run_all[];  // [kFusedWaves][NK] routing counts
+    __shared__ uint32_t s_last;
+    const int tid = threadIdx.x;
+    rank_tile<kFusedWaves, 1>(keys, a.N, a.scan.NK, a.nbits, (int64_t)blockIdx.x, run_all,
+                              a.local_rank, a.scan.tile_cnt, (int32_t*)a.scan.tile_flags);
+    // Publication of the tile: its counts and flags were stored at agent scope
+    // (written through to the coherence point), so completing them is enough
+    // for the last workgroup to see them; an agent-scope release fence would
+    // also write back every dirty line of this XCD's L2, which the previous
+    // kernel's streaming stores fill, and measured about 10 us per launch.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0) s_last = arrive_ticket(a.ticket, a.epoch) == (uint32_t)a.scan.tiles;
+    __syncthreads();
+    if (!s_last) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // every tile's counts visible
+    scan_tiles_body(a.scan);
+    if (tid == 0) __hip_atomic_store(a.ticket, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace
+
+hipError_t launch_route_fused(const RouteFusedArgs& a, hipStream_t s) {
+    if (a.scan.tiles <= 0 || a.scan.NK > kFusedMaxKeys) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)a.scan.tiles), block(kFusedThreads);
+    const size_t lds = sizeof(int32_t) * (size_t)kFusedWaves * a.scan.NK;
+    switch (a.kind) {
+        case KeyKind::Experts:
+            route_fused_kernel<<<grid, block, lds, s>>>(ExpertKeys{a.idx, a.E}, a);
+            break;
+        case KeyKind::Ranks:
+            route_fused_kernel<<<grid, block, lds, s>>>(RankKeys{a.idx, a.K, a.E, a.R, a.E / a.R},
+                                                        a);
+            break;
+        case KeyKind::Survivors:
+            route_fused_kernel<<<grid, block, lds, s>>>(
+                SurvivorKeys{a.idx, a.rank_slot, a.K, a.E, a.R, a.E / a.R}, a);
+            break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -15,69 +15,13 @@
 // bytes with one 16-byte store.
 #include "device_common.hpp"
 #include "internal.hpp"
+#include "rows_device.hpp"
 
 namespace moe {
 
 namespace {
 
 constexpr int kCopyThreads = 256;
-
-// Packed row of entry f, or -1 when the entry has no key or was dropped by the
-// capacity / row limit.
-__device__ __forceinline__ int entry_row(const SlotArgs& a, int64_t f) {
-    const int32_t lr = a.local_rank[f];
-    if (lr < 0) return -1;
-    const int32_t e = a.idx[f];
-    const int64_t slot = (int64_t)a.tile_base[(f / kTile) * a.E + e] + lr;
-    const int64_t base = a.cap > 0 ? (int64_t)e * a.cap : (int64_t)a.off[e];
-    if ((a.cap > 0 && slot >= a.cap) || base + slot >= a.packed_rows) return -1;
-    return (int)(base + slot);
-}
-
-template <int DMAX>
-__device__ __forceinline__ void broadcast_rows(int my_row, int (&rows)[DMAX]) {
-#pragma unroll
-    for (int d = 0; d < DMAX; ++d) rows[d] = readlane(my_row, d);
-}
-
-// Copy one row of nvec 16-byte vectors (already holding pass 0 in val) to up
-// to D destination rows; passes after the first reload from src.
-template <int DMAX, int VPT>
-__device__ __forceinline__ void store_row_copies(const char* src, int nvec, char* dst,
-                                                 int64_t row_bytes, const int (&rows)[DMAX], int D,
-                                                 u32x4 (&val)[VPT]) {
-    const int tid = threadIdx.x;
-    const int step = VPT * (int)blockDim.x;
-    for (int base = 0;;) {
-#pragma unroll
-        for (int d = 0; d < DMAX; ++d) {
-            if (d >= D) break;
-            if (rows[d] < 0) continue;
-            char* out = dst + (int64_t)rows[d] * row_bytes;
-#pragma unroll
-            for (int i = 0; i < VPT; ++i) {
-                const int v = base + tid + i * (int)blockDim.x;
-                if (v < nvec) st16_stream(out + (int64_t)v * 16, val[i]);
-            }
-        }
-        base += step;
-        if (base >= nvec) break;
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int v = base + tid + i * (int)blockDim.x;
-            if (v < nvec) val[i] = ld16_stream(src + (int64_t)v * 16);
-        }
-    }
-}
-
-template <int VPT>
-__device__ __forceinline__ void load_first_pass(const char* src, int nvec, u32x4 (&val)[VPT]) {
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-        const int v = threadIdx.x + i * (int)blockDim.x;
-        if (v < nvec) val[i] = ld16_stream(src + (int64_t)v * 16);
-    }
-}
 
 // ---------------------------------------------------------------------------
 // plain dispatch, bit copy (bf16 or f32)
@@ -92,7 +36,7 @@ __device__ __forceinline__ void scatter_copy_kernel_item(const ScatterArgs& a, i
     const char* src = (const char*)a.x + t * row_bytes;
 
     u32x4 val[VPT];
-    load_first_pass<VPT>(src, nvec, val);
+    load_first_pass<VPT>(src, nvec, val, (int)threadIdx.x, (int)blockDim.x);
 
     int my_row = -1;
     if (lane < K) my_row = entry_row(a.slot, t * K + lane);
@@ -102,45 +46,13 @@ __device__ __forceinline__ void scatter_copy_kernel_item(const ScatterArgs& a, i
     }
     int rows[DMAX];
     broadcast_rows<DMAX>(my_row, rows);
-    store_row_copies<DMAX, VPT>(src, nvec, (char*)a.packed, row_bytes, rows, K, val);
+    store_row_copies<DMAX, VPT>(src, nvec, (char*)a.packed, row_bytes, rows, K, val,
+                                (int)threadIdx.x, (int)blockDim.x);
 }
 
 // ---------------------------------------------------------------------------
 // plain dispatch, fused blockwise fp8 pack (bf16 in)
 // ---------------------------------------------------------------------------
-
-// Pack 16 bf16 values (two 16-byte vectors) of one lane; the 8 lanes of a
-// 128-element block agree on amax and the scale.
-__device__ __forceinline__ void fp8_pack16(const u32x4& lo, const u32x4& hi, u32x4& q,
-                                           float& scale) {
-    float v[16];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        v[2 * j] = bf16lo(lo[j]);
-        v[2 * j + 1] = bf16hi(lo[j]);
-        v[8 + 2 * j] = bf16lo(hi[j]);
-        v[8 + 2 * j + 1] = bf16hi(hi[j]);
-    }
-    float amax = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(v[j]));
-    amax = group8_max(amax);
-    scale = 1.0f;
-    if (amax > kE4m3Max) {
-        // q = e4m3(clamp((x * 448) / amax)); x * 448 is exact for bf16 x and the
-        // quotient is a correctly rounded f32 division.
-        scale = amax / kE4m3Max;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const float n = v[j] * kE4m3Max;
-            const float qv = n / amax;
-            v[j] = fminf(fmaxf(qv, -kE4m3Max), kE4m3Max);
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-        q[j] = pack_e4m3x4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]);
-}
 
 template <int DMAX, int UPT>
 __device__ __forceinline__ void scatter_fp8_kernel_item(const ScatterArgs& a, int64_t t) {
@@ -208,7 +120,7 @@ __device__ __forceinline__ void recv_copy_kernel_item(const RecvArgs& a, int64_t
     const char* src = (const char*)a.x + t * row_bytes;
 
     u32x4 val[VPT];
-    load_first_pass<VPT>(src, nvec, val);
+    load_first_pass<VPT>(src, nvec, val, (int)threadIdx.x, (int)blockDim.x);
 
     int my_row = -1;
     if (lane < R) {
@@ -225,7 +137,8 @@ __device__ __forceinline__ void recv_copy_kernel_item(const RecvArgs& a, int64_t
     }
     int rows[DMAX];
     broadcast_rows<DMAX>(my_row, rows);
-    store_row_copies<DMAX, VPT>(src, nvec, (char*)a.recv_x, row_bytes, rows, R, val);
+    store_row_copies<DMAX, VPT>(src, nvec, (char*)a.recv_x, row_bytes, rows, R, val,
+                                (int)threadIdx.x, (int)blockDim.x);
 }
 
 // ---------------------------------------------------------------------------

@@ -85,7 +85,9 @@ const char* moe_last_error(void);
 
 /* Bytes of device workspace that moe_route_count, moe_dispatch and (with
  * R > 0) moe_dedup_dispatch need for these sizes.  The workspace needs no
- * initialisation and may be reused by consecutive calls on one stream. */
+ * initialisation and may be reused by consecutive calls on one stream, also
+ * from a captured graph.  Calls that may run at the same time (other streams)
+ * need workspaces of their own: the routing keeps an arrival counter in it. */
 size_t moe_workspace_size(int64_t T, int K, int E, int R);
 
 /* Routing histogram and exclusive scan ("cco + flydsl dispatch/combine",

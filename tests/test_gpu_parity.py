@@ -387,3 +387,68 @@ def test_grid_stride_wrap_past_max_grid():
     eo, ew = oracle.combine(plain["packed"], "bf16", plain["tok_map"], w, "f32")
     _check_combine(host(out), eo, "f32")
     np.testing.assert_array_equal(host(ow), ew)
+
+
+# ---------------------------------------------------------------------------
+# one-launch routing: the arrival ticket lives in the caller's workspace
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fill", [0x00, 0xFF, 0xA5, "random"])
+def test_routing_any_workspace_contents(fill):
+    """The workspace needs no initialisation: whatever it holds (including a
+    ticket left by an earlier call), every call counts its own tiles."""
+    T, K, E = 5000, 8, 256
+    rng = np.random.default_rng(31)
+    idx = _mixed_idx(rng, T, K, E)
+    ws = moe.workspace(T, K, E)
+    if fill == "random":
+        ws.copy_(torch.from_numpy(rng.integers(0, 256, ws.numel(), dtype=np.uint8)).to(DEV))
+    else:
+        ws.fill_(fill)
+    rc, ro, rs = oracle.route_count(idx, E)
+    idx_d = dev(idx)
+    note(f"routing workspace fill={fill}")
+    for _ in range(3):
+        cnt, off, st = moe.route_count(idx_d, E, ws=ws)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(cnt), rc)
+        np.testing.assert_array_equal(host(off), ro)
+        np.testing.assert_array_equal(host(st), rs)
+
+
+def test_dispatch_graph_replays():
+    """A captured dispatch replays with the same launch arguments each time;
+    every replay, with eager launches on the same workspace in between, must
+    give the eager result."""
+    T, K, E, H = 3000, 8, 64, 256
+    rng = np.random.default_rng(37)
+    idx = _mixed_idx(rng, T, K, E)
+    x = W.normal_x(rng, T, H, "bf16")
+    ref = oracle.dispatch(x, "bf16", idx, E, packed_dt="fp8")
+    x_d, idx_d = dev_bf16(x), dev(idx)
+    ws = moe.workspace(T, K, E)
+    o = moe._lib.alloc_dispatch(T, H, K, E, T * K, x_d.dtype, True, DEV)
+    other = moe._lib.alloc_dispatch(T, H, K, E, T * K, x_d.dtype, True, DEV)
+    note("dispatch graph capture")
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cs):
+        moe.dispatch(x_d, idx_d, E, fp8=True, out=o, ws=ws)   # warm up on the capture stream
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cs):
+            moe.dispatch(x_d, idx_d, E, fp8=True, out=o, ws=ws)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for t in (o.packed, o.scales, o.packed_src, o.tok_map, o.packed_cnt, o.packed_off, o.stats):
+            poison_(t)
+        note(f"dispatch graph replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        assert_dispatch_equal(o, ref, fp8=True)
+        for t in (other.packed, other.scales, other.packed_src, other.tok_map, other.packed_cnt,
+                  other.packed_off, other.stats):
+            poison_(t)   # rows past the counts keep the poison, as in the oracle
+        moe.dispatch(x_d, idx_d, E, fp8=True, out=other, ws=ws)  # eager call in between
+        torch.cuda.synchronize()
+        assert_dispatch_equal(other, ref, fp8=True)
