@@ -11,9 +11,13 @@ namespace moe {
 // Packed row of entry f, or -1 when the entry has no key or was dropped by the
 // capacity / row limit.
 __device__ __forceinline__ int entry_row(const SlotArgs& a, int64_t f) {
+    // Both loads in flight together (e is only used once lr says it is valid);
+    // the empty asm keeps the compiler from sinking the idx load under the
+    // branch, which would cost a second memory round trip.
     const int32_t lr = a.local_rank[f];
+    int32_t e = a.idx[f];
+    asm volatile("" : "+v"(e));
     if (lr < 0) return -1;
-    const int32_t e = a.idx[f];
     const int64_t slot = (int64_t)a.tile_base[(f / kTile) * a.E + e] + lr;
     const int64_t base = a.cap > 0 ? (int64_t)e * a.cap : (int64_t)a.off[e];
     if ((a.cap > 0 && slot >= a.cap) || base + slot >= a.packed_rows || base + slot < 0) return -1;

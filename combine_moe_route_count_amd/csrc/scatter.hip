@@ -27,7 +27,7 @@ constexpr int kCopyThreads = 256;
 // plain dispatch, bit copy (bf16 or f32)
 // ---------------------------------------------------------------------------
 template <int DMAX, int VPT>
-__device__ __forceinline__ void scatter_copy_kernel_item(const ScatterArgs& a, int64_t t) {
+__device__ __forceinline__ void scatter_copy_kernel_item(const ScatterArgs& a, int64_t t, int nth) {
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
     const int K = a.slot.K;
@@ -36,7 +36,7 @@ __device__ __forceinline__ void scatter_copy_kernel_item(const ScatterArgs& a, i
     const char* src = (const char*)a.x + t * row_bytes;
 
     u32x4 val[VPT];
-    load_first_pass<VPT>(src, nvec, val, (int)threadIdx.x, (int)blockDim.x);
+    load_first_pass<VPT>(src, nvec, val, tid, nth);
 
     int my_row = -1;
     if (lane < K) my_row = entry_row(a.slot, t * K + lane);
@@ -46,8 +46,7 @@ __device__ __forceinline__ void scatter_copy_kernel_item(const ScatterArgs& a, i
     }
     int rows[DMAX];
     broadcast_rows<DMAX>(my_row, rows);
-    store_row_copies<DMAX, VPT>(src, nvec, (char*)a.packed, row_bytes, rows, K, val,
-                                (int)threadIdx.x, (int)blockDim.x);
+    store_row_copies<DMAX, VPT>(src, nvec, (char*)a.packed, row_bytes, rows, K, val, tid, nth);
 }
 
 // ---------------------------------------------------------------------------
@@ -55,14 +54,28 @@ __device__ __forceinline__ void scatter_copy_kernel_item(const ScatterArgs& a, i
 // ---------------------------------------------------------------------------
 
 template <int DMAX, int UPT>
-__device__ __forceinline__ void scatter_fp8_kernel_item(const ScatterArgs& a, int64_t t) {
+__device__ __forceinline__ void scatter_fp8_kernel_item(const ScatterArgs& a, int64_t t, int nth) {
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
     const int K = a.slot.K;
     const int64_t H = a.H;
     const int nunits = (int)(H / 16);          // 16 elements per lane-unit
     const int64_t nblk = H / kFp8Block;
+    const int step = UPT * nth;
     const char* src = (const char*)a.x + t * H * 2;
+
+    // the first pass of the row is in flight while the routing is looked up
+    u32x4 lo[UPT], hi[UPT];
+#pragma unroll
+    for (int i = 0; i < UPT; ++i) {
+        const int u = tid + i * nth;
+        lo[i] = u32x4{0, 0, 0, 0};
+        hi[i] = u32x4{0, 0, 0, 0};
+        if (u < nunits) {
+            lo[i] = ld16_stream(src + (int64_t)u * 32);
+            hi[i] = ld16_stream(src + (int64_t)u * 32 + 16);
+        }
+    }
 
     int my_row = -1;
     if (lane < K) my_row = entry_row(a.slot, t * K + lane);
@@ -71,20 +84,8 @@ __device__ __forceinline__ void scatter_fp8_kernel_item(const ScatterArgs& a, in
         if (my_row >= 0) a.packed_src[my_row] = (int32_t)t;
     }
     int rows[DMAX];
-    for (int base = 0; base < nunits; base += UPT * (int)blockDim.x) {
-        u32x4 lo[UPT], hi[UPT];
-#pragma unroll
-        for (int i = 0; i < UPT; ++i) {
-            const int u = base + tid + i * (int)blockDim.x;
-            if (u < nunits) {
-                lo[i] = ld16_stream(src + (int64_t)u * 32);
-                hi[i] = ld16_stream(src + (int64_t)u * 32 + 16);
-            } else {
-                lo[i] = u32x4{0, 0, 0, 0};
-                hi[i] = u32x4{0, 0, 0, 0};
-            }
-        }
-        if (base == 0) broadcast_rows<DMAX>(my_row, rows);
+    broadcast_rows<DMAX>(my_row, rows);
+    for (int base = 0;;) {
         u32x4 q[UPT];
         float s[UPT];
 #pragma unroll
@@ -97,11 +98,23 @@ __device__ __forceinline__ void scatter_fp8_kernel_item(const ScatterArgs& a, in
             float* sc = a.scales + (int64_t)rows[d] * nblk;
 #pragma unroll
             for (int i = 0; i < UPT; ++i) {
-                const int u = base + tid + i * (int)blockDim.x;
+                const int u = base + tid + i * nth;
                 if (u < nunits) {
                     st16_stream(out + (int64_t)u * 16, q[i]);
                     if ((u & 7) == 0) sc[u >> 3] = s[i];  // cached: L2 merges the 32-byte pieces of a scale row
                 }
+            }
+        }
+        base += step;
+        if (base >= nunits) break;
+#pragma unroll
+        for (int i = 0; i < UPT; ++i) {
+            const int u = base + tid + i * nth;
+            lo[i] = u32x4{0, 0, 0, 0};
+            hi[i] = u32x4{0, 0, 0, 0};
+            if (u < nunits) {
+                lo[i] = ld16_stream(src + (int64_t)u * 32);
+                hi[i] = ld16_stream(src + (int64_t)u * 32 + 16);
             }
         }
     }
@@ -111,7 +124,7 @@ __device__ __forceinline__ void scatter_fp8_kernel_item(const ScatterArgs& a, in
 // dedup stage 1: one copy of x[t] per (t, r) in the token's rank mask
 // ---------------------------------------------------------------------------
 template <int DMAX, int VPT>
-__device__ __forceinline__ void recv_copy_kernel_item(const RecvArgs& a, int64_t t) {
+__device__ __forceinline__ void recv_copy_kernel_item(const RecvArgs& a, int64_t t, int nth) {
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
     const int R = a.R;
@@ -120,7 +133,7 @@ __device__ __forceinline__ void recv_copy_kernel_item(const RecvArgs& a, int64_t
     const char* src = (const char*)a.x + t * row_bytes;
 
     u32x4 val[VPT];
-    load_first_pass<VPT>(src, nvec, val, (int)threadIdx.x, (int)blockDim.x);
+    load_first_pass<VPT>(src, nvec, val, tid, nth);
 
     int my_row = -1;
     if (lane < R) {
@@ -137,8 +150,7 @@ __device__ __forceinline__ void recv_copy_kernel_item(const RecvArgs& a, int64_t
     }
     int rows[DMAX];
     broadcast_rows<DMAX>(my_row, rows);
-    store_row_copies<DMAX, VPT>(src, nvec, (char*)a.recv_x, row_bytes, rows, R, val,
-                                (int)threadIdx.x, (int)blockDim.x);
+    store_row_copies<DMAX, VPT>(src, nvec, (char*)a.recv_x, row_bytes, rows, R, val, tid, nth);
 }
 
 // ---------------------------------------------------------------------------
@@ -146,7 +158,7 @@ __device__ __forceinline__ void recv_copy_kernel_item(const RecvArgs& a, int64_t
 // that rank (the same slots a plain dispatch of the surviving ids gives)
 // ---------------------------------------------------------------------------
 template <int KMAX, int VPT>
-__device__ __forceinline__ void expand_kernel_item(const ExpandArgs& a, int64_t t) {
+__device__ __forceinline__ void expand_kernel_item(const ExpandArgs& a, int64_t t, int nth) {
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
     const int K = a.slot.K;
@@ -176,11 +188,11 @@ __device__ __forceinline__ void expand_kernel_item(const ExpandArgs& a, int64_t 
         if (!any) continue;
         const int32_t srow = a.rank_slot[t * R + r];
         const char* src = (const char*)a.recv_x + (int64_t)srow * row_bytes;
-        for (int base = 0; base < nvec; base += VPT * (int)blockDim.x) {
+        for (int base = 0; base < nvec; base += VPT * nth) {
             u32x4 val[VPT];
 #pragma unroll
             for (int i = 0; i < VPT; ++i) {
-                const int v = base + tid + i * (int)blockDim.x;
+                const int v = base + tid + i * nth;
                 if (v < nvec) val[i] = ld16_stream(src + (int64_t)v * 16);
             }
 #pragma unroll
@@ -190,7 +202,7 @@ __device__ __forceinline__ void expand_kernel_item(const ExpandArgs& a, int64_t 
                 char* out = (char*)a.packed + (int64_t)rows[k] * row_bytes;
 #pragma unroll
                 for (int i = 0; i < VPT; ++i) {
-                    const int v = base + tid + i * (int)blockDim.x;
+                    const int v = base + tid + i * nth;
                     if (v < nvec) st16(out + (int64_t)v * 16, val[i]);
                 }
             }
@@ -201,34 +213,42 @@ __device__ __forceinline__ void expand_kernel_item(const ExpandArgs& a, int64_t 
 // ---------------------------------------------------------------------------
 // kernels: one source token per workgroup, grid-stride over tokens
 // ---------------------------------------------------------------------------
+// nth is the workgroup size, passed as an argument: blockDim.x comes from a
+// 16-bit field that gfx9 can only read with a vector load, which the compiler
+// repeats after every store it cannot prove disjoint and then waits for with
+// vmcnt(0), i.e. for every store in flight.
 template <int DMAX, int VPT>
-__global__ __launch_bounds__(kCopyThreads) void scatter_copy_kernel(ScatterArgs a) {
-    for (int64_t t = blockIdx.x; t < a.T; t += gridDim.x) scatter_copy_kernel_item<DMAX, VPT>(a, t);
+__global__ __launch_bounds__(kCopyThreads) void scatter_copy_kernel(ScatterArgs a, int nth) {
+    for (int64_t t = blockIdx.x; t < a.T; t += gridDim.x)
+        scatter_copy_kernel_item<DMAX, VPT>(a, t, nth);
 }
 template <int DMAX, int UPT>
-__global__ __launch_bounds__(kCopyThreads) void scatter_fp8_kernel(ScatterArgs a) {
-    for (int64_t t = blockIdx.x; t < a.T; t += gridDim.x) scatter_fp8_kernel_item<DMAX, UPT>(a, t);
+__global__ __launch_bounds__(kCopyThreads) void scatter_fp8_kernel(ScatterArgs a, int nth) {
+    for (int64_t t = blockIdx.x; t < a.T; t += gridDim.x)
+        scatter_fp8_kernel_item<DMAX, UPT>(a, t, nth);
 }
 template <int DMAX, int VPT>
-__global__ __launch_bounds__(kCopyThreads) void recv_copy_kernel(RecvArgs a) {
-    for (int64_t t = blockIdx.x; t < a.T; t += gridDim.x) recv_copy_kernel_item<DMAX, VPT>(a, t);
+__global__ __launch_bounds__(kCopyThreads) void recv_copy_kernel(RecvArgs a, int nth) {
+    for (int64_t t = blockIdx.x; t < a.T; t += gridDim.x) recv_copy_kernel_item<DMAX, VPT>(a, t, nth);
 }
 template <int KMAX, int VPT>
-__global__ __launch_bounds__(kCopyThreads) void expand_kernel(ExpandArgs a) {
-    for (int64_t t = blockIdx.x; t < a.T; t += gridDim.x) expand_kernel_item<KMAX, VPT>(a, t);
+__global__ __launch_bounds__(kCopyThreads) void expand_kernel(ExpandArgs a, int nth) {
+    for (int64_t t = blockIdx.x; t < a.T; t += gridDim.x) expand_kernel_item<KMAX, VPT>(a, t, nth);
 }
 
 // ---------------------------------------------------------------------------
 // fp8 dequantize: y = bf16(f32(q) * s[block])
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void fp8_dequant_kernel(const uint8_t* __restrict__ q,
+constexpr int kDequantThreads = 256;
+
+__global__ __launch_bounds__(kDequantThreads) void fp8_dequant_kernel(const uint8_t* __restrict__ q,
                                                           const float* __restrict__ scales,
                                                           int64_t units, int64_t H,
                                                           uint16_t* __restrict__ y) {
     const int64_t upr = H / 16;
     const int64_t nblk = H / kFp8Block;
-    for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < units;
-         u += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t stride = (int64_t)gridDim.x * kDequantThreads;
+    for (int64_t u = (int64_t)blockIdx.x * kDequantThreads + threadIdx.x; u < units; u += stride) {
         const int64_t row = u / upr;
         const int64_t col = (u - row * upr) * 16;
         const u32x4 v = ld16(q + row * H + col);
@@ -276,25 +296,25 @@ hipError_t by_dmax(int D, dim3 grid, int threads, const Args& a, hipStream_t s) 
 template <int D, int V>
 struct LaunchCopy {
     static void go(dim3 g, int th, const ScatterArgs& a, hipStream_t s) {
-        scatter_copy_kernel<D, V><<<g, dim3(th), 0, s>>>(a);
+        scatter_copy_kernel<D, V><<<g, dim3(th), 0, s>>>(a, th);
     }
 };
 template <int D, int V>
 struct LaunchFp8 {
     static void go(dim3 g, int th, const ScatterArgs& a, hipStream_t s) {
-        scatter_fp8_kernel<D, V><<<g, dim3(th), 0, s>>>(a);
+        scatter_fp8_kernel<D, V><<<g, dim3(th), 0, s>>>(a, th);
     }
 };
 template <int D, int V>
 struct LaunchRecv {
     static void go(dim3 g, int th, const RecvArgs& a, hipStream_t s) {
-        recv_copy_kernel<D, V><<<g, dim3(th), 0, s>>>(a);
+        recv_copy_kernel<D, V><<<g, dim3(th), 0, s>>>(a, th);
     }
 };
 template <int D, int V>
 struct LaunchExpand {
     static void go(dim3 g, int th, const ExpandArgs& a, hipStream_t s) {
-        expand_kernel<D, V><<<g, dim3(th), 0, s>>>(a);
+        expand_kernel<D, V><<<g, dim3(th), 0, s>>>(a, th);
     }
 };
 
@@ -331,10 +351,10 @@ hipError_t launch_fp8_dequant(const uint8_t* q, const float* scales, int64_t row
                               void* y, hipStream_t s) {
     const int64_t units = rows * (H / 16);
     if (units == 0) return hipSuccess;
-    int64_t blocks = (units + 255) / 256;
+    int64_t blocks = (units + kDequantThreads - 1) / kDequantThreads;
     if (blocks > 65536) blocks = 65536;
-    fp8_dequant_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(q, scales, units, H,
-                                                                    (uint16_t*)y);
+    fp8_dequant_kernel<<<dim3((unsigned)blocks), dim3(kDequantThreads), 0, s>>>(q, scales, units,
+                                                                                H, (uint16_t*)y);
     return hipGetLastError();
 }
 
