@@ -81,14 +81,15 @@ COPY_BYTES = 1 << 30   # calibration copy: 1 GiB read + 1 GiB written per launch
 
 
 def calibrate_copy(steps):
-    """A plain device-to-device copy of known size, profiled with the same
+    """The library's 16-byte streaming copy of known size, profiled with the same
     counters as the kernels so their KiB readings can be scaled to bytes."""
     import torch
+    import combine_moe_route_count_amd as moe
     a = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda:0")
     b = torch.empty_like(a)
     a.fill_(1)
     for _ in range(steps):
-        b.copy_(a)
+        moe.copy16(a, b)
     torch.cuda.synchronize()
     log(f"[bench] calibration copy of {COPY_BYTES} bytes x {steps} done")
 
@@ -107,8 +108,8 @@ def pmc_summary(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, out_json):
     scaled by what the same counters read for the 1 GiB calibration copy."""
     f = _pmc_rows(fetch_csv, "combine_kernel")
     wv = _pmc_rows(write_csv, "combine_kernel")
-    cf = _pmc_rows(cal_fetch_csv, "copy")
-    cw = _pmc_rows(cal_write_csv, "copy")
+    cf = _pmc_rows(cal_fetch_csv, "copy16_kernel")
+    cw = _pmc_rows(cal_write_csv, "copy16_kernel")
     cf_avg = statistics.mean(x for x in cf if x > 0)
     cw_avg = statistics.mean(x for x in cw if x > 0)
     fetch_scale = COPY_BYTES / cf_avg     # bytes per counter unit
@@ -155,6 +156,145 @@ def cpu_baseline(name, T_full, sample_T):
                       f"{T_full}/{sample_T} to one full call; expert step excluded"}
 
 
+def measure(moe, W, name, args, dev, graphs=True):
+    """Time dispatch+combine pairs of one workload; returns medians and spreads.
+
+    Pass 1 (the headline): HIP events on the launch stream around each
+    dispatch+combine pair, none between the two calls.  Pass 2 (breakdown): a
+    marker between dispatch and combine as well.  Pass 3: each pair replayed
+    from a captured HIP graph, its outputs checked against the eager ones."""
+    import numpy as np
+    import torch
+
+    d = W.make_inputs(name)
+    T, H, E, K = d["T"], d["H"], d["E"], d["K"]
+    fp8 = d["packed_dtype"] == "fp8"
+    assert d["x_dtype"] == "bf16"
+    log(f"[bench] workload {name}: T={T} H={H} E={E} K={K} fp8={fp8} sets={args.sets}")
+    x0 = torch.from_numpy(d["x"].view(np.int16)).view(torch.bfloat16).to(dev)
+    idx = torch.from_numpy(d["idx"]).to(dev)
+    w = torch.from_numpy(d["w"]).to(dev)
+    ws = moe.workspace(T, K, E, 0, dev)
+    sets = []
+    for s_ in range(args.sets):
+        x = x0.clone()
+        o = moe.dispatch(x, idx, E, fp8=fp8, ws=ws)
+        y = moe.fp8_dequant(o.packed, o.scales) if fp8 else o.packed.clone()
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        ow = torch.empty(T, dtype=torch.float32, device=dev)
+        sets.append(dict(x=x, o=o, y=y, out=out, ow=ow))
+    del x0
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, events=None):
+        st = sets[i % len(sets)]
+        if events is not None:
+            events[0].record(stream)
+        moe.dispatch(st["x"], idx, E, fp8=fp8, out=st["o"], ws=ws)
+        if events is not None and len(events) == 3:
+            events[1].record(stream)
+        moe.combine(st["y"], st["o"].tok_map, w, out=st["out"], out_weights=st["ow"])
+        if events is not None:
+            events[-1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"[bench] {name}: warmup {args.warmup} done")
+
+    n_ev = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_ev)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, ev[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    log(f"[bench] {name}: timed {args.steps} steps done")
+    pair_us = [ev[i][0].elapsed_time(ev[i][1]) * 1e3 for i in range(n_ev)]
+    wall_ms = (t1 - t0) * 1e3 / args.steps
+
+    evb = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_ev)]
+    for i in range(args.steps):
+        step(i, evb[i])
+    torch.cuda.synchronize()
+    disp_us = [evb[i][0].elapsed_time(evb[i][1]) * 1e3 for i in range(n_ev)]
+    comb_us = [evb[i][1].elapsed_time(evb[i][2]) * 1e3 for i in range(n_ev)]
+
+    # correctness spot check (identity expert telescopes: weights sum to 1)
+    st = sets[(args.steps - 1) % len(sets)]
+    assert int(st["o"].stats[1].item()) == 0 and int(st["o"].stats[0].item()) == 0
+    ow_err = float((st["ow"] - 1.0).abs().max().item())
+    assert ow_err < 1e-5, ow_err
+
+    graph_us = None
+    if graphs:
+        eager_out = [st_["out"].clone() for st_ in sets]
+        cs = torch.cuda.Stream(dev)
+        cs.wait_stream(stream)
+        gs = []
+        with torch.cuda.stream(cs):
+            for i in range(len(sets)):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=cs):
+                    step(i)
+                gs.append(g)
+        torch.cuda.synchronize()
+        for i in range(args.warmup):
+            gs[i % len(gs)].replay()
+        evg = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_ev)]
+        for i in range(args.steps):
+            evg[i][0].record(stream)
+            gs[i % len(gs)].replay()
+            evg[i][1].record(stream)
+        torch.cuda.synchronize()
+        graph_us = [evg[i][0].elapsed_time(evg[i][1]) * 1e3 for i in range(n_ev)]
+        for st_, ref in zip(sets, eager_out):
+            assert torch.equal(st_["out"].view(torch.int16), ref.view(torch.int16)), \
+                "graph replay output differs from the eager output"
+        log(f"[bench] {name}: graph replays done, outputs equal to eager")
+
+    # drop the first timed round (start transient)
+    tail = lambda v: v[1:] if len(v) > 2 else v
+    disp_b, comb_b = algorithmic_bytes(T, H, K, E, T * K, fp8=fp8)
+    r = dict(name=name, T=T, H=H, E=E, K=K, fp8=fp8, routing=d["workload"].routing,
+             pair_us=statistics.median(tail(pair_us)), pair_us_min=min(tail(pair_us)),
+             pair_us_std=statistics.pstdev(tail(pair_us)),
+             dispatch_us=statistics.median(tail(disp_us)), combine_us=statistics.median(tail(comb_us)),
+             combine_us_mean=statistics.mean(tail(comb_us)), wall_ms=wall_ms,
+             disp_b=disp_b, comb_b=comb_b)
+    if graph_us is not None:
+        r.update(graph_pair_us=statistics.median(tail(graph_us)), graph_pair_us_min=min(tail(graph_us)),
+                 graph_pair_us_std=statistics.pstdev(tail(graph_us)))
+    del sets
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return r
+
+
+def copy_ceiling(moe, dev, reps=10):
+    """GB/s (bytes read + written) of the library's 16-byte streaming copy of
+    1 GiB, on the same stream as the kernels."""
+    import torch
+    a = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(1)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(3):
+        moe.copy16(a, b)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+    for e in ev:
+        e[0].record(stream)
+        moe.copy16(a, b)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    us = statistics.median(e[0].elapsed_time(e[1]) * 1e3 for e in ev)
+    del a, b
+    torch.cuda.empty_cache()
+    return 2 * COPY_BYTES / (us * 1e-6) / 1e9
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -162,6 +302,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sets", type=int, default=3, help="rotating buffer sets")
     ap.add_argument("--workload", default="skewed_fp8")
+    ap.add_argument("--secondary", default="uniform_bf16",
+                    help="second workload reported inside the line ('none' to skip)")
+    ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay pass")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-sample", type=int, default=1024)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -179,7 +322,6 @@ def main():
               "sharding of this path is described in DESIGN.md and is not built.", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import combine_moe_route_count_amd as moe
@@ -192,95 +334,44 @@ def main():
         calibrate_copy(args.steps)
         return
     name = args.workload
-    d = W.make_inputs(name)
-    T, H, E, K = d["T"], d["H"], d["E"], d["K"]
-    fp8 = d["packed_dtype"] == "fp8"
-    assert d["x_dtype"] == "bf16"
-    log(f"[bench] workload {name}: T={T} H={H} E={E} K={K} fp8={fp8} sets={args.sets}")
-
-    x0 = torch.from_numpy(d["x"].view(np.int16)).view(torch.bfloat16).to(dev)
-    idx = torch.from_numpy(d["idx"]).to(dev)
-    w = torch.from_numpy(d["w"]).to(dev)
-    N_rows = T * K
-    ws = moe.workspace(T, K, E, 0, dev)
-    sets = []
-    for s in range(args.sets):
-        x = x0.clone()
-        o = moe.dispatch(x, idx, E, fp8=fp8, ws=ws)
-        y = moe.fp8_dequant(o.packed, o.scales) if fp8 else o.packed.clone()
-        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-        ow = torch.empty(T, dtype=torch.float32, device=dev)
-        sets.append(dict(x=x, o=o, y=y, out=out, ow=ow))
-    del x0
-    torch.cuda.synchronize()
-
-    stream = torch.cuda.current_stream(dev)
-
-    def step(i, events=None):
-        st = sets[i % len(sets)]
-        if events is not None:
-            events[0].record(stream)
-        moe.dispatch(st["x"], idx, E, fp8=fp8, out=st["o"], ws=ws)
-        if events is not None and len(events) == 3:
-            events[1].record(stream)
-        moe.combine(st["y"], st["o"].tok_map, w, out=st["out"], out_weights=st["ow"])
-        if events is not None:
-            events[-1].record(stream)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    log(f"[bench] warmup {args.warmup} done")
-
-    # pass 1 (the headline): HIP events on the launch stream around each
-    # dispatch+combine pair, none between the two calls
-    n_ev = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_ev)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i, ev[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    log(f"[bench] timed {args.steps} steps done")
-    pair_us = [ev[i][0].elapsed_time(ev[i][1]) * 1e3 for i in range(n_ev)]
-    wall_ms = (t1 - t0) * 1e3 / args.steps
-
-    # pass 2 (breakdown): a marker between dispatch and combine as well
-    evb = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_ev)]
-    for i in range(args.steps):
-        step(i, evb[i])
-    torch.cuda.synchronize()
-    disp_us = [evb[i][0].elapsed_time(evb[i][1]) * 1e3 for i in range(n_ev)]
-    comb_us = [evb[i][1].elapsed_time(evb[i][2]) * 1e3 for i in range(n_ev)]
-
-    # drop the first timed round (start transient), report the median
-    med = lambda v: statistics.median(v[1:] if len(v) > 2 else v)
-    d_us, c_us, t_us = med(disp_us), med(comb_us), med(pair_us)
-
-    # correctness spot check of the last step (identity expert telescopes)
-    st = sets[(args.steps - 1) % len(sets)]
-    assert int(st["o"].stats[1].item()) == 0 and int(st["o"].stats[0].item()) == 0
-    ow_err = float((st["ow"] - 1.0).abs().max().item())
-    assert ow_err < 1e-5, ow_err
-
-    disp_b, comb_b = algorithmic_bytes(T, H, K, E, N_rows, fp8=fp8)
+    r = measure(moe, W, name, args, dev, graphs=not args.no_graph)
+    t_us, d_us, c_us = r["pair_us"], r["dispatch_us"], r["combine_us"]
+    disp_b, comb_b = r["disp_b"], r["comb_b"]
     total_b = disp_b + comb_b
     gbs = total_b / (t_us * 1e-6) / 1e9
     comb_gbs = comb_b / (c_us * 1e-6) / 1e9
     disp_gbs = disp_b / (d_us * 1e-6) / 1e9
-    c_avg = statistics.mean(comb_us[1:] if n_ev > 2 else comb_us)
+    c_avg = r["combine_us_mean"]
     roof_gbs = comb_b / (c_avg * 1e-6) / 1e9
     khash = source_hash(COMBINE_SOURCES)
     traffic = stored_traffic(khash)
     log(f"[bench] dispatch {d_us:.1f} us ({disp_gbs:.0f} GB/s)  combine {c_us:.1f} us "
         f"({comb_gbs:.0f} GB/s)  total {t_us:.1f} us ({gbs:.0f} GB/s, {100 * gbs / HBM_PEAK_GBS:.1f}% "
-        f"of peak)  wall {wall_ms * 1e3:.1f} us/step")
+        f"of peak)  wall {r['wall_ms'] * 1e3:.1f} us/step")
+
+    sec = None
+    if args.secondary != "none" and args.secondary != name:
+        s2 = measure(moe, W, args.secondary, args, dev, graphs=not args.no_graph)
+        tb2 = s2["disp_b"] + s2["comb_b"]
+        g2 = tb2 / (s2["pair_us"] * 1e-6) / 1e9
+        sec = {"workload": s2["name"], "T": s2["T"], "H": s2["H"], "E": s2["E"], "K": s2["K"],
+               "routing": s2["routing"], "payload": "fp8_e4m3+f32_scale_per_128" if s2["fp8"] else "bf16",
+               "pair_us": round(s2["pair_us"], 2), "pair_us_min": round(s2["pair_us_min"], 2),
+               "pair_us_std": round(s2["pair_us_std"], 2), "dispatch_us": round(s2["dispatch_us"], 2),
+               "combine_us": round(s2["combine_us"], 2),
+               "algorithmic_bytes": {"dispatch": s2["disp_b"], "combine": s2["comb_b"]},
+               "achieved_gbps": round(g2, 1), "pct_hbm_peak": round(100 * g2 / HBM_PEAK_GBS, 2)}
+        if "graph_pair_us" in s2:
+            sec["graph_pair_us"] = round(s2["graph_pair_us"], 2)
+        log(f"[bench] secondary {s2['name']}: {s2['pair_us']:.1f} us ({g2:.0f} GB/s)")
+
+    copy_gbs = copy_ceiling(moe, dev)
+    log(f"[bench] 16-byte streaming copy of 1 GiB: {copy_gbs:.0f} GB/s (read + write)")
 
     cpu = None
     if not args.no_cpu:
         log(f"[bench] cpu oracle baseline on T={args.cpu_sample} sample ...")
-        cpu = cpu_baseline(name, T, args.cpu_sample)
+        cpu = cpu_baseline(name, r["T"], args.cpu_sample)
         log(f"[bench] cpu oracle: {cpu['value']} us/call on {cpu['cores']} threads")
 
     line = {
@@ -290,21 +381,25 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(wall_ms, 4),
+        "ms_per_step": round(r["wall_ms"], 4),
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": name, "T": T, "H": H, "E": E, "K": K,
-                   "routing": "zipf1.2" if d["workload"].routing == "zipf" else "uniform",
-                   "payload": "fp8_e4m3+f32_scale_per_128" if fp8 else "bf16",
+        "config": {"workload": name, "T": r["T"], "H": r["H"], "E": r["E"], "K": r["K"],
+                   "routing": "zipf1.2" if r["routing"] == "zipf" else "uniform",
+                   "payload": "fp8_e4m3+f32_scale_per_128" if r["fp8"] else "bf16",
                    "combine": "bf16_in_f32_acc_bf16_out", "layout": "compact",
                    "buffer_sets": args.sets},
         "achieved_gbps": round(gbs, 1),
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-        "pair_us_min": round(min(pair_us[1:] if n_ev > 2 else pair_us), 2),
-        "pair_us_std": round(statistics.pstdev(pair_us[1:] if n_ev > 2 else pair_us), 2),
+        "pct_copy_ceiling": round(100 * gbs / copy_gbs, 2),
+        "copy_ceiling_gbps": round(copy_gbs, 1),
+        "pair_us_min": round(r["pair_us_min"], 2),
+        "pair_us_std": round(r["pair_us_std"], 2),
+        "graph_pair_us": round(r["graph_pair_us"], 2) if "graph_pair_us" in r else None,
+        "graph_pair_us_min": round(r["graph_pair_us_min"], 2) if "graph_pair_us" in r else None,
         "dispatch_us": round(d_us, 2),
         "combine_us": round(c_us, 2),
         "dispatch_gbps": round(disp_gbs, 1),
@@ -313,6 +408,7 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(roof_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "bytes_per_launch": comb_b,
                      "avg_launch_us": round(c_avg, 2)},
+        "secondary": sec,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

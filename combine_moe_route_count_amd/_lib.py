@@ -66,8 +66,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                                        _P, _P, _P, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _SZ,
                                        _P]
     lib.moe_fp8_dequant.argtypes = [_P, _P, _I64, _I64, _P, _P]
+    lib.moe_copy16.argtypes = [_P, _P, _I64, _P]
     for fn in ("moe_route_count", "moe_dispatch", "moe_combine", "moe_dedup_dispatch",
-               "moe_fp8_dequant"):
+               "moe_fp8_dequant", "moe_copy16"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -257,3 +258,11 @@ def fp8_dequant(q: torch.Tensor, scales: torch.Tensor, y: Optional[torch.Tensor]
     y = torch.empty((rows, H), dtype=torch.bfloat16, device=q.device) if y is None else y
     _check(load().moe_fp8_dequant(ptr(q), ptr(scales), rows, H, ptr(y), _stream(q.device)))
     return y
+
+
+def copy16(src: torch.Tensor, dst: torch.Tensor) -> torch.Tensor:
+    """dst <- src bytes with the library's 16-byte streaming copy (the copy ceiling)."""
+    n = src.numel() * src.element_size()
+    assert dst.numel() * dst.element_size() >= n
+    _check(load().moe_copy16(ptr(src), ptr(dst), n, _stream(src.device)))
+    return dst

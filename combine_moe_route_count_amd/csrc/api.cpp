@@ -459,3 +459,17 @@ MOE_API int moe_fp8_dequant(const uint8_t* q, const float* scales, int64_t rows,
     MOE_HIP(moe::launch_fp8_dequant(q, scales, rows, H, y, (hipStream_t)stream), "moe_fp8_dequant");
     return ok();
 }
+
+MOE_API int moe_copy16(const void* src, void* dst, int64_t bytes, void* stream) {
+    if (bytes < 0 || bytes % 16 != 0)
+        return fail(MOE_ERR_INVALID_ARG, "bytes=%lld must be a non-negative multiple of 16",
+                    (long long)bytes);
+    if (bytes > 0 && (!src || !dst)) return fail(MOE_ERR_INVALID_ARG, "src or dst is NULL");
+    if ((src && !aligned(src, 16)) || (dst && !aligned(dst, 16)))
+        return fail(MOE_ERR_INVALID_ARG, "src and dst must be 16-byte aligned");
+    const uintptr_t a = (uintptr_t)src, b = (uintptr_t)dst;
+    if (bytes > 0 && a < b + (uintptr_t)bytes && b < a + (uintptr_t)bytes)
+        return fail(MOE_ERR_INVALID_ARG, "src and dst overlap");
+    MOE_HIP(moe::launch_copy16(src, dst, bytes, (hipStream_t)stream), "moe_copy16");
+    return ok();
+}

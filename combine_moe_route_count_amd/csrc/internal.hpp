@@ -127,6 +127,7 @@ hipError_t launch_route_fused(const RouteFusedArgs& a, hipStream_t s);
 
 hipError_t launch_fp8_dequant(const uint8_t* q, const float* scales, int64_t rows, int64_t H,
                               void* y, hipStream_t s);
+hipError_t launch_copy16(const void* src, void* dst, int64_t bytes, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // combine

@@ -30,6 +30,14 @@ __device__ __forceinline__ void broadcast_rows(int my_row, int (&rows)[DMAX]) {
     for (int d = 0; d < DMAX; ++d) rows[d] = readlane(my_row, d);
 }
 
+// Marks loaded registers as settled: the compiler waits for their loads once,
+// before the empty asm, and sees plain values afterwards.
+template <int N>
+__device__ __forceinline__ void settle(u32x4 (&v)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) asm volatile("" : "+v"(v[i]));
+}
+
 // Copy one row of nvec 16-byte vectors (already holding pass 0 in val) to up
 // to D destination rows; passes after the first reload from src.
 template <int DMAX, int VPT>
@@ -38,6 +46,11 @@ __device__ __forceinline__ void store_row_copies(const char* src, int nvec, char
                                                  u32x4 (&val)[VPT], int tid, int nthreads) {
     const int step = VPT * nthreads;
     for (int base = 0;;) {
+        // Every store below is conditional and reads loaded registers; without
+        // this one explicit use the compiler loses count of the loads at each
+        // join and waits for vmcnt(0) before every store, i.e. for the previous
+        // stores too.  The empty asm takes the wait once, here.
+        settle(val);
 #pragma unroll
         for (int d = 0; d < DMAX; ++d) {
             if (d >= D) break;

@@ -193,8 +193,10 @@ __device__ __forceinline__ void expand_kernel_item(const ExpandArgs& a, int64_t 
 #pragma unroll
             for (int i = 0; i < VPT; ++i) {
                 const int v = base + tid + i * nth;
+                val[i] = u32x4{0, 0, 0, 0};
                 if (v < nvec) val[i] = ld16_stream(src + (int64_t)v * 16);
             }
+            settle(val);
 #pragma unroll
             for (int k = 0; k < KMAX; ++k) {
                 if (k >= K) break;
@@ -271,6 +273,32 @@ __global__ __launch_bounds__(kDequantThreads) void fp8_dequant_kernel(const uint
         }
         st16(y + row * H + col, o0);
         st16(y + row * H + col + 8, o1);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 16-byte streaming copy: the plain copy the row movers are measured against
+// ---------------------------------------------------------------------------
+constexpr int kStreamThreads = 256;
+constexpr int kStreamUnroll = 4;   // 16-byte vectors per lane in flight
+
+__global__ __launch_bounds__(kStreamThreads) void copy16_kernel(const u32x4* __restrict__ src,
+                                                                u32x4* __restrict__ dst,
+                                                                int64_t nvec) {
+    const int64_t per_block = (int64_t)kStreamThreads * kStreamUnroll;
+    const int64_t stride = (int64_t)gridDim.x * per_block;
+    for (int64_t base = (int64_t)blockIdx.x * per_block; base < nvec; base += stride) {
+        u32x4 v[kStreamUnroll];
+#pragma unroll
+        for (int i = 0; i < kStreamUnroll; ++i) {
+            const int64_t j = base + i * kStreamThreads + threadIdx.x;
+            if (j < nvec) v[i] = ld16_stream(src + j);
+        }
+#pragma unroll
+        for (int i = 0; i < kStreamUnroll; ++i) {
+            const int64_t j = base + i * kStreamThreads + threadIdx.x;
+            if (j < nvec) st16_stream(dst + j, v[i]);
+        }
     }
 }
 
@@ -355,6 +383,17 @@ hipError_t launch_fp8_dequant(const uint8_t* q, const float* scales, int64_t row
     if (blocks > 65536) blocks = 65536;
     fp8_dequant_kernel<<<dim3((unsigned)blocks), dim3(kDequantThreads), 0, s>>>(q, scales, units,
                                                                                 H, (uint16_t*)y);
+    return hipGetLastError();
+}
+
+hipError_t launch_copy16(const void* src, void* dst, int64_t bytes, hipStream_t s) {
+    const int64_t nvec = bytes / 16;
+    if (nvec == 0) return hipSuccess;
+    const int64_t per_block = (int64_t)kStreamThreads * kStreamUnroll;
+    int64_t blocks = (nvec + per_block - 1) / per_block;
+    if (blocks > kMaxGrid) blocks = kMaxGrid;  // one pass per workgroup up to 64 GiB
+    copy16_kernel<<<dim3((unsigned)blocks), dim3(kStreamThreads), 0, s>>>(
+        (const u32x4*)src, (u32x4*)dst, nvec);
     return hipGetLastError();
 }
 

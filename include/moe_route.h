@@ -184,6 +184,11 @@ int moe_dedup_dispatch(const void* x, moe_dtype x_dt, int64_t T, int64_t H, cons
 int moe_fp8_dequant(const uint8_t* q, const float* scales, int64_t rows, int64_t H, void* y,
                     void* stream);
 
+/* Plain device copy with 16-byte streaming loads and stores: the copy ceiling
+ * the row movers are compared with (a measurement helper, not on the path).
+ *   src, dst  device, 16-byte aligned, not overlapping; bytes % 16 == 0. */
+int moe_copy16(const void* src, void* dst, int64_t bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

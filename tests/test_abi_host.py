@@ -107,6 +107,13 @@ res["dequant"] = {
     "rows_neg": [lib.moe_fp8_dequant(A, A, -1, 128, A, None), lib.moe_last_error().decode()],
     "scales_null": [lib.moe_fp8_dequant(A, None, 4, 128, A, None), lib.moe_last_error().decode()],
 }
+res["copy16"] = {
+    "bytes_odd": [lib.moe_copy16(A, P(0x300000), 24, None), lib.moe_last_error().decode()],
+    "bytes_neg": [lib.moe_copy16(A, P(0x300000), -16, None), lib.moe_last_error().decode()],
+    "src_null": [lib.moe_copy16(None, P(0x300000), 32, None), lib.moe_last_error().decode()],
+    "unaligned": [lib.moe_copy16(A8, P(0x300000), 32, None), lib.moe_last_error().decode()],
+    "overlap": [lib.moe_copy16(A, P(0x100010), 64, None), lib.moe_last_error().decode()],
+}
 res["route"] = {
     "cnt_null": [lib.moe_route_count(A, 10, 2, 4, None, A, None, WS, 1 << 20, None),
                  lib.moe_last_error().decode()],
@@ -178,5 +185,7 @@ def test_dedup_and_helpers_argument_errors():
         assert st == (WORKSPACE if case == "ws_small" else INVALID), (case, st, msg)
     for case, (st, msg) in _res()["dequant"].items():
         assert st == INVALID, (case, st, msg)
+    for case, (st, msg) in _res()["copy16"].items():
+        assert st == INVALID and msg, (case, st, msg)
     r = _res()["route"]
     assert r["cnt_null"][0] == INVALID and r["ws_small"][0] == WORKSPACE

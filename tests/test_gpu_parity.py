@@ -452,3 +452,17 @@ def test_dispatch_graph_replays():
         moe.dispatch(x_d, idx_d, E, fp8=True, out=other, ws=ws)  # eager call in between
         torch.cuda.synchronize()
         assert_dispatch_equal(other, ref, fp8=True)
+
+
+@pytest.mark.parametrize("nbytes", [0, 16, 4096 + 16, (1 << 20) + 48])
+def test_copy16_bytes(nbytes):
+    """The copy-ceiling helper moves the bytes exactly (grid tail included)."""
+    rng = np.random.default_rng(nbytes)
+    src = torch.from_numpy(rng.integers(0, 256, nbytes + 16, dtype=np.uint8)).to(DEV)
+    dst = torch.full((nbytes + 16,), 0xA5, dtype=torch.uint8, device=DEV)
+    note(f"copy16 bytes={nbytes}")
+    moe.copy16(src[:nbytes], dst[:nbytes])
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:nbytes], src[:nbytes])
+    assert bool((dst[nbytes:] == 0xA5).all()), "copy wrote past its end"
+

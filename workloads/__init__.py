@@ -14,9 +14,11 @@ CTA-independent local kernels" (MoonEP PR 34, "Measured impact" table)):
   prefill     T=4096  H=7168  E=256 K=8  uniform routing, bf16 x, padded layout
   skewed_fp8  T=8192  H=7168  E=256 K=8  Zipf(1.2) routing, bf16 x, fp8 payload
   dedup       T=16384 H=4096  E=64  K=6  R=8 virtual ranks, uniform routing, f32 x
+  uniform_bf16 T=8192 H=7168  E=256 K=8  uniform routing, bf16 x and payload (the
+              skewed_fp8 shape without the skew and the fp8 pack; seed 4 as well)
 
 Random draws, in this order, from numpy.random.Generator(PCG64(seed)) with
-seed = the workload number (1..5):
+seed = the workload number (1..5; uniform_bf16 shares seed 4):
   1. expert permutation (Zipf only)
   2. routing (distinct top-K experts per token)
   3. gate logits  -> weights = softmax over the K picks, in float64, cast to float32
@@ -64,6 +66,8 @@ WORKLOADS = {
     "prefill": Workload("prefill", 3, 4096, 7168, 256, 8, "uniform", "bf16", "bf16", "padded", "identity"),
     "skewed_fp8": Workload("skewed_fp8", 4, 8192, 7168, 256, 8, "zipf", "bf16", "fp8", "compact", "dequant"),
     "dedup": Workload("dedup", 5, 16384, 4096, 64, 6, "uniform", "f32", "f32", "compact", "identity", R=8),
+    "uniform_bf16": Workload("uniform_bf16", 4, 8192, 7168, 256, 8, "uniform", "bf16", "bf16", "compact",
+                             "identity"),
 }
 
 
