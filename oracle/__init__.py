@@ -54,6 +54,7 @@ def _load():
         "oracle_route_count": [P, I64, I32, I32, P, P, P],
         "oracle_dispatch": [P, I32, I64, I64, P, I32, I32, I64, I64, P, I32, P, P, P, P, P, P],
         "oracle_combine": [P, I32, I64, I64, P, P, I64, I32, P, I32, P],
+        "oracle_combine_fp8": [P, P, I64, I64, P, P, I64, I32, P, I32, P],
         "oracle_dedup_dispatch": [P, I32, I64, I64, P, I32, I32, I32, P, I64, P, P, P, P, I64,
                                   I64, P, P, P, P, P, P],
         "oracle_dedup_combine": [P, I32, I64, I64, P, P, P, I64, I32, I32, I32, P, I64, P, P,
@@ -151,6 +152,24 @@ def combine(y: np.ndarray, y_dt: str, tok_map: np.ndarray, w: np.ndarray, out_dt
     out = np.empty((T, H), NP_DT[od])
     ow = np.empty(T, np.float32)
     _load().oracle_combine(_p(y), yd, y_rows, H, _p(tok_map), _p(w), T, K, _p(out), od, _p(ow))
+    return out, ow
+
+
+def combine_fp8(q: np.ndarray, scales, tok_map: np.ndarray, w: np.ndarray, out_dt: str):
+    """Combine of fp8 expert outputs: q uint8 [rows,H] e4m3 codes, scales f32
+    [rows,H/128] or None (direct cast).  (out [T,H] bf16 bits or f32, out_weights [T])."""
+    od = DT[out_dt]
+    q = _c(q, np.uint8)
+    sc = None if scales is None else _c(scales, np.float32)
+    tok_map = _c(tok_map, np.int64)
+    w = _c(w, np.float32)
+    T, K = tok_map.shape
+    y_rows, H = q.shape
+    assert H % 128 == 0 and (sc is None or sc.shape == (y_rows, H // 128))
+    out = np.empty((T, H), NP_DT[od])
+    ow = np.empty(T, np.float32)
+    _load().oracle_combine_fp8(_p(q), _p(sc), y_rows, H, _p(tok_map), _p(w), T, K, _p(out), od,
+                               _p(ow))
     return out, ow
 
 

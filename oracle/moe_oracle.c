@@ -45,6 +45,9 @@
  *            with the product and the sum each rounded to f32 (no fused
  *            multiply-add).  out_weights[t] is the f32 sum of the weights of
  *            the entries that contributed, in the same order.
+ *   R-comb8  fp8 expert outputs: v = f32(e4m3(q)) * s with the block's f32
+ *            scale (1 when no scales are given), one rounded multiply and no
+ *            bf16 step, then the R-comb reduction over v.
  *   R-dedup  virtual rank of expert e is e / (E/R), computed only for valid e.
  *            Recv rows: one per (t, r in M[t]) in t order per rank; rows past
  *            recv_rows are dropped with every entry they carry.  Surviving
@@ -342,6 +345,51 @@ int oracle_combine(const void* y, int y_dt, int64_t y_rows, int64_t H, const int
             float wk = w[t * K + k];
             for (int64_t h = 0; h < H; ++h) {
                 float p = wk * load_elem(y, y_dt, row * H + h);
+                acc[h] = acc[h] + p;
+            }
+            ws = ws + wk;
+        }
+        for (int64_t h = 0; h < H; ++h) {
+            if (out_dt == ORC_BF16)
+                ((uint16_t*)out)[t * H + h] = f32_to_bf16(acc[h]);
+            else
+                ((float*)out)[t * H + h] = acc[h];
+        }
+        if (out_weights)
+            out_weights[t] = ws;
+        free(acc);
+    }
+    return 0;
+}
+
+/* Combine of fp8 expert outputs (reading R-comb8): y arrives as e4m3 codes q
+ * with one f32 scale per 128-element block of each row ([mori#448] commit
+ * "Port mori's Fp8BlockwiseQuant ...": the receiving side dequantizes fp8 times
+ * the block's scale and accumulates); scales == NULL is the direct cast
+ * ([mori#448] commit "... make_combine_scatter ..."), i.e. every scale 1.
+ * Each element is dequantized inside the reduce as v = f32(q) * s, one f32
+ * multiply with no bf16 rounding in between, and then combined exactly as in
+ * oracle_combine: acc = acc + (w * v) for k ascending. */
+int oracle_combine_fp8(const uint8_t* q, const float* scales, int64_t y_rows, int64_t H,
+                       const int64_t* tok_map, const float* w, int64_t T, int K, void* out,
+                       int out_dt, float* out_weights) {
+    const int64_t nblk = H / FP8_BLOCK;
+    int64_t t;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (t = 0; t < T; ++t) {
+        float* acc = (float*)malloc((size_t)H * sizeof(float));
+        float ws = 0.0f;
+        for (int64_t h = 0; h < H; ++h)
+            acc[h] = 0.0f;
+        for (int k = 0; k < K; ++k) {
+            int64_t row = tok_map[t * K + k];
+            if (row < 0 || row >= y_rows)
+                continue;
+            float wk = w[t * K + k];
+            for (int64_t h = 0; h < H; ++h) {
+                float s = scales ? scales[row * nblk + h / FP8_BLOCK] : 1.0f;
+                float v = e4m3_to_f32(q[row * H + h]) * s;
+                float p = wk * v;
                 acc[h] = acc[h] + p;
             }
             ws = ws + wk;
