@@ -35,8 +35,9 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(T, H, K, E, N_rows, fp8=True, y_bytes=2, out_bytes=2):
-    """Bytes the method must move per call (metadata once, rows once)."""
+def algorithmic_bytes(T, H, K, E, N_rows, fp8=True, y_bytes=2, out_bytes=2, y_fp8=False):
+    """Bytes the method must move per call (metadata once, rows once).  y_fp8:
+    the combine reads e4m3 expert outputs with one f32 scale per 128 elements."""
     idx = T * K * 4
     tok_map = T * K * 8
     w = T * K * 4
@@ -47,7 +48,7 @@ def algorithmic_bytes(T, H, K, E, N_rows, fp8=True, y_bytes=2, out_bytes=2):
         rows_w = N_rows * H * 2
     meta_d = idx + tok_map + N_rows * 4 + E * 4 * 2   # idx in, tok_map/packed_src/cnt/off out
     disp = x + rows_w + meta_d
-    comb_rows = N_rows * H * y_bytes
+    comb_rows = N_rows * H + N_rows * (H // 128) * 4 if y_fp8 else N_rows * H * y_bytes
     comb = comb_rows + T * H * out_bytes + tok_map + w + T * 4
     return disp, comb
 
@@ -156,11 +157,12 @@ def cpu_baseline(name, T_full, sample_T):
                       f"{T_full}/{sample_T} to one full call; expert step excluded"}
 
 
-def measure(moe, W, name, args, dev, graphs=True):
+def measure(moe, W, name, args, dev, graphs=True, y_fp8=False):
     """Time dispatch+combine pairs of one workload; returns medians and spreads.
 
     Pass 1 (the headline): HIP events on the launch stream around each
-    dispatch+combine pair, none between the two calls.  Pass 2 (breakdown): a
+    dispatch+combine pair, none between the two calls.  y_fp8: the combine takes
+    the fp8 packed rows and scales themselves (moe_combine_fp8, identity expert).  Pass 2 (breakdown): a
     marker between dispatch and combine as well.  Pass 3: each pair replayed
     from a captured HIP graph, its outputs checked against the eager ones."""
     import numpy as np
@@ -169,8 +171,8 @@ def measure(moe, W, name, args, dev, graphs=True):
     d = W.make_inputs(name)
     T, H, E, K = d["T"], d["H"], d["E"], d["K"]
     fp8 = d["packed_dtype"] == "fp8"
-    assert d["x_dtype"] == "bf16"
-    log(f"[bench] workload {name}: T={T} H={H} E={E} K={K} fp8={fp8} sets={args.sets}")
+    assert d["x_dtype"] == "bf16" and (fp8 or not y_fp8)
+    log(f"[bench] workload {name}: T={T} H={H} E={E} K={K} fp8={fp8} y_fp8={y_fp8} sets={args.sets}")
     x0 = torch.from_numpy(d["x"].view(np.int16)).view(torch.bfloat16).to(dev)
     idx = torch.from_numpy(d["idx"]).to(dev)
     w = torch.from_numpy(d["w"]).to(dev)
@@ -179,7 +181,10 @@ def measure(moe, W, name, args, dev, graphs=True):
     for s_ in range(args.sets):
         x = x0.clone()
         o = moe.dispatch(x, idx, E, fp8=fp8, ws=ws)
-        y = moe.fp8_dequant(o.packed, o.scales) if fp8 else o.packed.clone()
+        if y_fp8:
+            y = None
+        else:
+            y = moe.fp8_dequant(o.packed, o.scales) if fp8 else o.packed.clone()
         out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
         ow = torch.empty(T, dtype=torch.float32, device=dev)
         sets.append(dict(x=x, o=o, y=y, out=out, ow=ow))
@@ -194,7 +199,11 @@ def measure(moe, W, name, args, dev, graphs=True):
         moe.dispatch(st["x"], idx, E, fp8=fp8, out=st["o"], ws=ws)
         if events is not None and len(events) == 3:
             events[1].record(stream)
-        moe.combine(st["y"], st["o"].tok_map, w, out=st["out"], out_weights=st["ow"])
+        if y_fp8:
+            moe.combine_fp8(st["o"].packed, st["o"].scales, st["o"].tok_map, w, out=st["out"],
+                            out_weights=st["ow"])
+        else:
+            moe.combine(st["y"], st["o"].tok_map, w, out=st["out"], out_weights=st["ow"])
         if events is not None:
             events[-1].record(stream)
 
@@ -257,7 +266,7 @@ def measure(moe, W, name, args, dev, graphs=True):
 
     # drop the first timed round (start transient)
     tail = lambda v: v[1:] if len(v) > 2 else v
-    disp_b, comb_b = algorithmic_bytes(T, H, K, E, T * K, fp8=fp8)
+    disp_b, comb_b = algorithmic_bytes(T, H, K, E, T * K, fp8=fp8, y_fp8=y_fp8)
     r = dict(name=name, T=T, H=H, E=E, K=K, fp8=fp8, routing=d["workload"].routing,
              pair_us=statistics.median(tail(pair_us)), pair_us_min=min(tail(pair_us)),
              pair_us_std=statistics.pstdev(tail(pair_us)),
@@ -305,6 +314,8 @@ def main():
     ap.add_argument("--secondary", default="uniform_bf16",
                     help="second workload reported inside the line ('none' to skip)")
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay pass")
+    ap.add_argument("--no-fp8-combine", action="store_true",
+                    help="skip the line that feeds the fp8 rows straight to moe_combine_fp8")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-sample", type=int, default=1024)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -365,6 +376,21 @@ def main():
             sec["graph_pair_us"] = round(s2["graph_pair_us"], 2)
         log(f"[bench] secondary {s2['name']}: {s2['pair_us']:.1f} us ({g2:.0f} GB/s)")
 
+    f8 = None
+    if r["fp8"] and not args.no_fp8_combine:
+        s3 = measure(moe, W, name, args, dev, graphs=False, y_fp8=True)
+        tb3 = s3["disp_b"] + s3["comb_b"]
+        g3 = tb3 / (s3["pair_us"] * 1e-6) / 1e9
+        f8 = {"workload": name, "combine": "fp8_e4m3+f32_scale_per_128_in_f32_acc_bf16_out",
+              "pair_us": round(s3["pair_us"], 2), "pair_us_min": round(s3["pair_us_min"], 2),
+              "pair_us_std": round(s3["pair_us_std"], 2), "dispatch_us": round(s3["dispatch_us"], 2),
+              "combine_us": round(s3["combine_us"], 2),
+              "algorithmic_bytes": {"dispatch": s3["disp_b"], "combine": s3["comb_b"]},
+              "achieved_gbps": round(g3, 1), "pct_hbm_peak": round(100 * g3 / HBM_PEAK_GBS, 2),
+              "combine_gbps": round(s3["comb_b"] / (s3["combine_us"] * 1e-6) / 1e9, 1)}
+        log(f"[bench] fp8-input combine: pair {s3['pair_us']:.1f} us, combine {s3['combine_us']:.1f} us "
+            f"({f8['combine_gbps']:.0f} GB/s)")
+
     copy_gbs = copy_ceiling(moe, dev)
     log(f"[bench] 16-byte streaming copy of 1 GiB: {copy_gbs:.0f} GB/s (read + write)")
 
@@ -409,6 +435,7 @@ def main():
                      "traffic": traffic, "bytes_per_launch": comb_b,
                      "avg_launch_us": round(c_avg, 2)},
         "secondary": sec,
+        "fp8_combine": f8,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

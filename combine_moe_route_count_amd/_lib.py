@@ -67,8 +67,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                                        _P]
     lib.moe_fp8_dequant.argtypes = [_P, _P, _I64, _I64, _P, _P]
     lib.moe_copy16.argtypes = [_P, _P, _I64, _P]
+    lib.moe_combine_fp8.argtypes = [_P, _P, _I64, _I64, _P, _P, _I64, _I32, _P, _I32, _P, _P]
     for fn in ("moe_route_count", "moe_dispatch", "moe_combine", "moe_dedup_dispatch",
-               "moe_fp8_dequant", "moe_copy16"):
+               "moe_fp8_dequant", "moe_copy16", "moe_combine_fp8"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -197,6 +198,23 @@ def combine(y: torch.Tensor, tok_map: torch.Tensor, w: torch.Tensor, E: int = 0,
     _check(load().moe_combine(ptr(y), dtype_code(y.dtype), y_rows, H, ptr(tok_map), ptr(w), T, K,
                               E, ctypes.byref(plan) if plan is not None else None, ptr(out),
                               dtype_code(out.dtype), ptr(out_weights), _stream(dev)))
+    return out, out_weights
+
+
+def combine_fp8(q: torch.Tensor, scales: Optional[torch.Tensor], tok_map: torch.Tensor,
+                w: torch.Tensor, out_dtype: torch.dtype = torch.bfloat16,
+                out: Optional[torch.Tensor] = None, out_weights: Optional[torch.Tensor] = None,
+                want_weights: bool = True):
+    """Combine of fp8 expert outputs: q uint8 [rows,H] e4m3 codes, scales f32
+    [rows,H/128] or None (direct cast); out [T,H] = sum_k w * (f32(q) * s)."""
+    y_rows, H = q.shape
+    T, K = tok_map.shape
+    dev = q.device
+    out = torch.empty((T, H), dtype=out_dtype, device=dev) if out is None else out
+    if want_weights and out_weights is None:
+        out_weights = torch.empty(T, dtype=torch.float32, device=dev)
+    _check(load().moe_combine_fp8(ptr(q), ptr(scales), y_rows, H, ptr(tok_map), ptr(w), T, K,
+                                  ptr(out), dtype_code(out.dtype), ptr(out_weights), _stream(dev)))
     return out, out_weights
 
 

@@ -367,6 +367,40 @@ MOE_API int moe_combine(const void* y, moe_dtype y_dt, int64_t y_rows, int64_t H
     return ok();
 }
 
+MOE_API int moe_combine_fp8(const uint8_t* q, const float* scales, int64_t y_rows, int64_t H,
+                            const int64_t* tok_map, const float* w, int64_t T, int K, void* out,
+                            moe_dtype out_dt, float* out_weights, void* stream) {
+    if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T must be >= 0");
+    if (K < 1 || K > 16) return fail(MOE_ERR_INVALID_ARG, "K=%d must be in [1,16]", K);
+    if (out_dt != MOE_BF16 && out_dt != MOE_F32)
+        return fail(MOE_ERR_INVALID_ARG, "out dtype must be MOE_BF16 or MOE_F32");
+    MOE_TRY(check_H(H, true));
+    if (y_rows < 0) return fail(MOE_ERR_INVALID_ARG, "y_rows must be >= 0");
+    MOE_TRY(check_rows_ptr(q, y_rows, "q"));
+    if (scales && !aligned(scales, 4)) return fail(MOE_ERR_INVALID_ARG, "scales is not 4-byte aligned");
+    MOE_TRY(check_rows_ptr(out, T, "out"));
+    if (T > 0 && (!tok_map || !w)) return fail(MOE_ERR_INVALID_ARG, "tok_map and w must be non-NULL");
+    if (tok_map && !aligned(tok_map, 8)) return fail(MOE_ERR_INVALID_ARG, "tok_map is not 8-byte aligned");
+    if (w && !aligned(w, 4)) return fail(MOE_ERR_INVALID_ARG, "w is not 4-byte aligned");
+    if (out_weights && !aligned(out_weights, 4))
+        return fail(MOE_ERR_INVALID_ARG, "out_weights is not 4-byte aligned");
+    moe::CombineArgs a{};
+    a.y = q;
+    a.y_fp8 = true;
+    a.y_scales = scales;
+    a.y_rows = y_rows;
+    a.H = H;
+    a.tok_map = tok_map;
+    a.w = w;
+    a.T = T;
+    a.K = K;
+    a.out = out;
+    a.out_f32 = out_dt == MOE_F32;
+    a.out_weights = out_weights;
+    MOE_HIP(moe::launch_combine(a, (hipStream_t)stream), "moe_combine_fp8");
+    return ok();
+}
+
 MOE_API int moe_dedup_dispatch(const void* x, moe_dtype x_dt, int64_t T, int64_t H,
                                const int32_t* idx, int K, int E, int R, void* recv_x,
                                int64_t recv_rows, int32_t* recv_cnt, int32_t* recv_off,

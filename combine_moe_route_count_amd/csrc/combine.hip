@@ -110,9 +110,9 @@ struct Chunking {
     int C;       // units per chunk
 };
 
-inline Chunking chunking(int64_t H) {
+inline Chunking chunking(int64_t H, int unit_elems = 8) {
     Chunking ch;
-    ch.units = (int)(H / 8);
+    ch.units = (int)(H / unit_elems);
     ch.nch = (ch.units + kChunkUnits - 1) / kChunkUnits;
     ch.C = (ch.units + ch.nch - 1) / ch.nch;
     return ch;
@@ -164,6 +164,79 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(CombineArgs a, in
     for (int64_t wi = blockIdx.x; wi < items; wi += gridDim.x) {
         const int64_t t = wi / nch;
         combine_item<YF32, OF32, KMAX>(a, t, (int)(wi - t * nch), C);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// combine of fp8 expert outputs: v = f32(q) * s (the row's block scale, 1 for
+// the direct cast), then acc = acc + w_k * v for k ascending.  A lane-unit is
+// 16 elements: one 16-byte load of codes per row (the same bytes in flight as
+// the bf16 form's 8 elements) plus the row's scale, dequantized two codes per
+// v_cvt_pk_f32_fp8 inside the reduce.
+// ---------------------------------------------------------------------------
+template <bool OF32, int KMAX>
+__device__ __forceinline__ void combine_fp8_item(const CombineArgs& a, int64_t t, int c, int C) {
+    const int64_t H = a.H;
+    const int units = (int)(H / 16);
+    const int64_t nblk = H / kFp8Block;
+    int rows[KMAX];
+    float w[KMAX];
+    token_entries<KMAX>(a, t, rows, w);
+
+    const int u = c * C + (int)threadIdx.x;
+    if ((int)threadIdx.x < C && u < units) {
+        const uint8_t* q = (const uint8_t*)a.y;
+        u32x4 code[KMAX];
+        float scl[KMAX];
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            if (rows[k] < 0) continue;
+            code[k] = ld16_stream(q + (int64_t)rows[k] * H + (int64_t)u * 16);
+            scl[k] = a.y_scales ? a.y_scales[(int64_t)rows[k] * nblk + u / (kFp8Block / 16)] : 1.0f;
+        }
+        float acc[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[j] = 0.0f;
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            if (rows[k] < 0) continue;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                float v[4];
+                unpack_e4m3x2<false>(code[k][d], v[0], v[1]);
+                unpack_e4m3x2<true>(code[k][d], v[2], v[3]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float dq = v[j] * scl[k];
+                    const float p = w[k] * dq;
+                    acc[4 * d + j] = acc[4 * d + j] + p;
+                }
+            }
+        }
+        float lo[8], hi[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            lo[j] = acc[j];
+            hi[j] = acc[8 + j];
+        }
+        store_unit<OF32>(a.out, t, H, (int64_t)u * 16, lo);
+        store_unit<OF32>(a.out, t, H, (int64_t)u * 16 + 8, hi);
+    }
+    if (c == 0 && threadIdx.x == 0 && a.out_weights) {
+        float s = 0.0f;
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k)
+            if (rows[k] >= 0) s = s + w[k];
+        a.out_weights[t] = s;
+    }
+}
+
+template <bool OF32, int KMAX>
+__global__ __launch_bounds__(kCombThreads) void combine_fp8_kernel(CombineArgs a, int C, int nch) {
+    const int64_t items = a.T * nch;
+    for (int64_t wi = blockIdx.x; wi < items; wi += gridDim.x) {
+        const int64_t t = wi / nch;
+        combine_fp8_item<OF32, KMAX>(a, t, (int)(wi - t * nch), C);
     }
 }
 
@@ -341,11 +414,29 @@ void by_k(const CombineArgs& a, hipStream_t s) {
 #undef MOE_K_CASE
 }
 
+template <bool OF32, int KMAX>
+void fp8_go(const CombineArgs& a, hipStream_t s) {
+    const Chunking ch = chunking(a.H, 16);
+    combine_fp8_kernel<OF32, KMAX>
+        <<<item_grid(a.T * ch.nch), dim3(threads_for(ch.C)), 0, s>>>(a, ch.C, ch.nch);
+}
+
+template <bool OF32>
+void fp8_by_k(const CombineArgs& a, hipStream_t s) {
+    if (a.K <= 2) fp8_go<OF32, 2>(a, s);
+    else if (a.K <= 4) fp8_go<OF32, 4>(a, s);
+    else if (a.K <= 8) fp8_go<OF32, 8>(a, s);
+    else fp8_go<OF32, 16>(a, s);
+}
+
 }  // namespace
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
     if (a.T == 0) return hipSuccess;
-    if (a.y_f32) {
+    if (a.y_fp8) {
+        if (a.out_f32) fp8_by_k<true>(a, s);
+        else fp8_by_k<false>(a, s);
+    } else if (a.y_f32) {
         if (a.out_f32) by_k<true, true>(a, s);
         else by_k<true, false>(a, s);
     } else {

@@ -136,6 +136,8 @@ hipError_t launch_copy16(const void* src, void* dst, int64_t bytes, hipStream_t 
 struct CombineArgs {
     const void* y;
     bool y_f32;
+    bool y_fp8;              // e4m3 codes, dequantized with y_scales (NULL: scale 1)
+    const float* y_scales;   // [y_rows, H/128]
     int64_t y_rows, H;
     const int64_t* tok_map;
     const float* w;

@@ -178,6 +178,25 @@ int moe_dedup_dispatch(const void* x, moe_dtype x_dt, int64_t T, int64_t H, cons
                        int32_t* packed_off, int32_t* packed_src, int64_t* tok_map,
                        int32_t* stats, void* ws, size_t ws_bytes, void* stream);
 
+/* Combine of fp8 expert outputs ("Draft: cco + flydsl dispatch/combine",
+ * commit "Port mori's Fp8BlockwiseQuant ...": the receiving side dequantizes
+ * fp8 times the block scale and accumulates; commit "... make_combine_scatter
+ * ...": the direct-cast variant without scales).  For t, and k ascending with
+ * 0 <= tok_map[t,k] < y_rows:
+ *   v   = f32(e4m3(q[row][h])) * scales[row][h/128]    (scale 1 if scales NULL;
+ *         one rounded f32 multiply, no bf16 step)
+ *   acc = acc + w[t,k] * v                             (each op rounded, no FMA)
+ *   out[t] = acc as bf16 (nearest even) or f32; out_weights[t] = sum of those w.
+ *   q        uint8 [y_rows,H] e4m3fn codes, 16-byte aligned; H % 128 == 0
+ *   scales   f32 [y_rows,H/128], or NULL for the direct cast
+ *   tok_map, w, T, K, out, out_dt, out_weights as for moe_combine.
+ * With scales NULL (or all 1) the result equals moe_combine on the bf16
+ * decoding of q.  Errors: MOE_ERR_INVALID_ARG for the checks of moe_combine
+ * and H % 128 != 0; enqueues nothing on error.  The dedup plan is not taken. */
+int moe_combine_fp8(const uint8_t* q, const float* scales, int64_t y_rows, int64_t H,
+                    const int64_t* tok_map, const float* w, int64_t T, int K, void* out,
+                    moe_dtype out_dt, float* out_weights, void* stream);
+
 /* Blockwise fp8 dequantize (the inverse step of Fp8BlockwiseQuant):
  * y = bf16(f32(q) * scales[row][h/128]), rounded to nearest even.
  *   q  uint8 [rows,H], scales f32 [rows,H/128], y out bf16 [rows,H]; H % 128 == 0. */

@@ -114,6 +114,18 @@ res["copy16"] = {
     "unaligned": [lib.moe_copy16(A8, P(0x300000), 32, None), lib.moe_last_error().decode()],
     "overlap": [lib.moe_copy16(A, P(0x100010), 64, None), lib.moe_last_error().decode()],
 }
+def c8(**kw):
+    a = dict(q=A, sc=A, yr=10, H=128, tm=A, w=A, T=5, K=2, out=A, odt=0, ow=None)
+    a.update(kw)
+    st = lib.moe_combine_fp8(a["q"], a["sc"], a["yr"], a["H"], a["tm"], a["w"], a["T"], a["K"],
+                             a["out"], a["odt"], a["ow"], None)
+    return [st, lib.moe_last_error().decode()]
+
+res["combine_fp8"] = {
+    "H64": c8(H=64), "K0": c8(K=0), "K17": c8(K=17), "out_fp8": c8(odt=2), "q_null": c8(q=None),
+    "q_unaligned": c8(q=A8), "scales_unaligned": c8(sc=P(0x100002)), "tm_null": c8(tm=None),
+    "out_unaligned": c8(out=A8), "Tneg": c8(T=-1), "y_rows_neg": c8(yr=-1),
+}
 res["route"] = {
     "cnt_null": [lib.moe_route_count(A, 10, 2, 4, None, A, None, WS, 1 << 20, None),
                  lib.moe_last_error().decode()],
@@ -185,6 +197,8 @@ def test_dedup_and_helpers_argument_errors():
         assert st == (WORKSPACE if case == "ws_small" else INVALID), (case, st, msg)
     for case, (st, msg) in _res()["dequant"].items():
         assert st == INVALID, (case, st, msg)
+    for case, (st, msg) in _res()["combine_fp8"].items():
+        assert st == INVALID and msg, (case, st, msg)
     for case, (st, msg) in _res()["copy16"].items():
         assert st == INVALID and msg, (case, st, msg)
     r = _res()["route"]

@@ -466,3 +466,71 @@ def test_copy16_bytes(nbytes):
     assert torch.equal(dst[:nbytes], src[:nbytes])
     assert bool((dst[nbytes:] == 0xA5).all()), "copy wrote past its end"
 
+
+# ---------------------------------------------------------------------------
+# combine of fp8 expert outputs
+# ---------------------------------------------------------------------------
+
+def _fp8_codes(rng, shape):
+    q = rng.integers(0, 256, size=shape, dtype=np.uint8)
+    q[(q & 0x7F) == 0x7F] = 0x38          # no NaN codes
+    return q
+
+
+@pytest.mark.parametrize("out_dt", ["bf16", "f32"])
+@pytest.mark.parametrize("K,H,T,scaled", [(1, 128, 37, True), (3, 384, 300, True), (8, 7168, 129, True),
+                                          (8, 7168, 65, False), (16, 256, 513, True), (6, 4096, 1000, False)])
+def test_combine_fp8_random(out_dt, K, H, T, scaled):
+    rng = np.random.default_rng(K * 1000 + H + T)
+    rows = max(T * K // 2, K)
+    q = _fp8_codes(rng, (rows, H))
+    sc = (rng.random((rows, H // 128)) * 8 + 2.0 ** -6).astype(np.float32) if scaled else None
+    tm = rng.integers(-1, rows, size=(T, K)).astype(np.int64)
+    tm[rng.random((T, K)) < 0.02] = rows + 3          # out of range: skipped
+    w = rng.standard_normal((T, K)).astype(np.float32)
+    note(f"combine_fp8 K={K} H={H} T={T} scaled={scaled} out={out_dt}")
+    odt = torch.float32 if out_dt == "f32" else torch.bfloat16
+    out = torch.empty((T, H), dtype=odt, device=DEV)
+    ow = torch.empty(T, dtype=torch.float32, device=DEV)
+    poison_(out)
+    poison_(ow)
+    moe.combine_fp8(dev(q), dev(sc) if scaled else None, dev(tm), dev(w), out=out, out_weights=ow)
+    torch.cuda.synchronize()
+    exp, ew = oracle.combine_fp8(q, sc, tm, w, out_dt)
+    exact = _check_combine(host(out), exp, out_dt)
+    np.testing.assert_array_equal(host(ow), ew)
+    print(f"bit-exact={exact}")
+
+
+def test_combine_fp8_direct_cast_equals_bf16_combine():
+    """No scales: the fp8 combine equals the bf16 combine of the decoded rows
+    (both on the GPU, bitwise)."""
+    rng = np.random.default_rng(7)
+    rows, H, T, K = 3000, 1024, 700, 8
+    q = _fp8_codes(rng, (rows, H))
+    tm = rng.integers(-1, rows, size=(T, K)).astype(np.int64)
+    w = rng.random((T, K)).astype(np.float32)
+    qd = dev(q)
+    yb = qd.view(torch.float8_e4m3fn).to(torch.bfloat16)
+    note("combine_fp8 direct cast vs bf16 combine")
+    a, aw = moe.combine_fp8(qd, None, dev(tm), dev(w))
+    b, bw = moe.combine(yb, dev(tm), dev(w))
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.equal(aw, bw)
+
+
+def test_combine_fp8_skewed_full():
+    """The metric workload with the fp8 packed rows themselves as the expert
+    output (identity expert, no dequantize pass)."""
+    d = W.make_inputs("skewed_fp8")
+    x = W.inject_outliers(d["x"], np.arange(0, d["T"], 97), 1000.0)
+    note("combine_fp8 skewed_fp8 full T=8192")
+    o = gpu_dispatch(dev_bf16(x), d["idx"], d["E"], fp8=True)
+    out, ow = moe.combine_fp8(o.packed, o.scales, o.tok_map, dev(d["w"]))
+    torch.cuda.synchronize()
+    ref = oracle.dispatch(x, "bf16", d["idx"], d["E"], packed_dt="fp8")
+    exp, ew = oracle.combine_fp8(ref["packed"], ref["scales"], ref["tok_map"], d["w"], "bf16")
+    assert _check_combine(host(out), exp, "bf16")
+    np.testing.assert_array_equal(host(ow), ew)
+
