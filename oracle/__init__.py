@@ -52,7 +52,8 @@ def _load():
     P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     sigs = {
         "oracle_route_count": [P, I64, I32, I32, P, P, P],
-        "oracle_dispatch": [P, I32, I64, I64, P, I32, I32, I64, I64, P, I32, P, P, P, P, P, P],
+        "oracle_dispatch": [P, I32, P, I64, I64, P, I32, I32, I64, I64, P, I32, P, P, P, P, P, P],
+        "oracle_dispatch_replay": [P, I32, P, I64, I64, P, I32, I64, P, I32, P],
         "oracle_combine": [P, I32, I64, I64, P, P, I64, I32, P, I32, P],
         "oracle_combine_fp8": [P, P, I64, I64, P, P, I64, I32, P, I32, P],
         "oracle_dedup_dispatch": [P, I32, I64, I64, P, I32, I32, I32, P, I64, P, P, P, P, I64,
@@ -113,17 +114,22 @@ def _rows_needed(idx, E, cap):
 
 
 def dispatch(x: np.ndarray, x_dt: str, idx: np.ndarray, E: int, cap: int = 0,
-             packed_rows: int | None = None, packed_dt: str | None = None) -> dict:
-    """Plain dispatch.  x: uint16 bf16 bits or float32 [T,H].  Returns a dict of
-    packed [rows,H] (poisoned where not written), scales f32 [rows,H/128] (fp8
-    only), packed_cnt [E], packed_off [E+1], packed_src [rows] (poisoned where
-    not written), tok_map int64 [T,K], stats [3]."""
+             packed_rows: int | None = None, packed_dt: str | None = None,
+             x_scales: np.ndarray | None = None) -> dict:
+    """Plain dispatch.  x: uint16 bf16 bits, float32, or (x_dt "fp8") uint8 e4m3
+    codes with x_scales f32 [T,H/128] [T,H].  Returns a dict of packed [rows,H]
+    (poisoned where not written), scales f32 [rows,H/128] (fp8 only), packed_cnt
+    [E], packed_off [E+1], packed_src [rows] (poisoned where not written),
+    tok_map int64 [T,K], stats [3]."""
     idx = _c(idx, np.int32)
     T, K = idx.shape
     xd = DT[x_dt]
     pd = DT[packed_dt or x_dt]
     if pd != xd and not (pd == FP8 and xd == BF16):
         raise ValueError("packed dtype must equal x dtype, or be fp8 from bf16")
+    if (xd == FP8) != (x_scales is not None):
+        raise ValueError("x_scales go with fp8 input, and only with it")
+    xs = None if x_scales is None else _c(x_scales, np.float32)
     x = _c(x, NP_DT[xd])
     H = x.shape[1]
     rows = _rows_needed(idx, E, cap) if packed_rows is None else int(packed_rows)
@@ -135,10 +141,35 @@ def dispatch(x: np.ndarray, x_dt: str, idx: np.ndarray, E: int, cap: int = 0,
     packed_src = np.full(rows, POISON_I32, np.int32)
     tok_map = np.empty((T, K), np.int64)
     stats = np.zeros(3, np.int32)
-    _load().oracle_dispatch(_p(x), xd, T, H, _p(idx), K, E, cap, rows, _p(packed), pd, _p(scales),
-                            _p(packed_cnt), _p(packed_off), _p(packed_src), _p(tok_map), _p(stats))
+    _load().oracle_dispatch(_p(x), xd, _p(xs), T, H, _p(idx), K, E, cap, rows, _p(packed), pd,
+                            _p(scales), _p(packed_cnt), _p(packed_off), _p(packed_src),
+                            _p(tok_map), _p(stats))
     return dict(packed=packed, scales=scales, packed_cnt=packed_cnt, packed_off=packed_off,
                 packed_src=packed_src, tok_map=tok_map, stats=stats)
+
+
+def dispatch_replay(x: np.ndarray, x_dt: str, tok_map: np.ndarray, packed_rows: int,
+                    packed_dt: str | None = None, x_scales: np.ndarray | None = None) -> dict:
+    """Replay dispatch on a cached tok_map [T,K]: packed [rows,H] and (fp8)
+    scales [rows,H/128], poisoned where not written."""
+    tok_map = _c(tok_map, np.int64)
+    T, K = tok_map.shape
+    xd = DT[x_dt]
+    pd = DT[packed_dt or x_dt]
+    if pd != xd and not (pd == FP8 and xd == BF16):
+        raise ValueError("packed dtype must equal x dtype, or be fp8 from bf16")
+    if (xd == FP8) != (x_scales is not None):
+        raise ValueError("x_scales go with fp8 input, and only with it")
+    xs = None if x_scales is None else _c(x_scales, np.float32)
+    x = _c(x, NP_DT[xd])
+    H = x.shape[1]
+    rows = int(packed_rows)
+    eb = {BF16: 2, F32: 4, FP8: 1}[pd]
+    packed = np.full((rows, H * eb), POISON_BYTE, np.uint8).view(NP_DT[pd])
+    scales = np.full((rows, H // 128 * 4), POISON_BYTE, np.uint8).view(np.float32) if pd == FP8 else None
+    _load().oracle_dispatch_replay(_p(x), xd, _p(xs), T, H, _p(tok_map), K, rows, _p(packed), pd,
+                                   _p(scales))
+    return dict(packed=packed, scales=scales)
 
 
 def combine(y: np.ndarray, y_dt: str, tok_map: np.ndarray, w: np.ndarray, out_dt: str):

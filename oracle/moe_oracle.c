@@ -48,6 +48,11 @@
  *   R-comb8  fp8 expert outputs: v = f32(e4m3(q)) * s with the block's f32
  *            scale (1 when no scales are given), one rounded multiply and no
  *            bf16 step, then the R-comb reduction over v.
+ *   R-prequant  fp8 input (e4m3 codes with one f32 scale per 128-element
+ *            block) is dispatched byte for byte and each token's scale row is
+ *            forwarded unchanged to every packed row of the token.
+ *   R-replay a cached tok_map is reused as it stands: entries inside
+ *            [0, packed_rows) get their token's row, nothing else is written.
  *   R-dedup  virtual rank of expert e is e / (E/R), computed only for valid e.
  *            Recv rows: one per (t, r in M[t]) in t order per rank; rows past
  *            recv_rows are dropped with every entry they carry.  Surviving
@@ -268,10 +273,12 @@ static int64_t assign_slots(const int32_t* idx, const uint8_t* keep, int64_t T, 
 }
 
 /* Copy (or fp8-pack) the source row of every entry with tok_map >= 0.
- * src_row_of(f) is x[t] for plain dispatch and the recv row for dedup. */
-static void copy_rows(const void* src, int src_dt, int64_t H, const int64_t* src_row,
-                      const int64_t* tok_map, int64_t N, void* packed, int packed_dt,
-                      float* scales) {
+ * src_row_of(f) is x[t] for plain dispatch and the recv row for dedup.  An
+ * fp8 source (pre-quantized input) is copied byte for byte and its scale row
+ * src_scales[s] is forwarded verbatim (reading R-prequant). */
+static void copy_rows(const void* src, int src_dt, const float* src_scales, int64_t H,
+                      const int64_t* src_row, const int64_t* tok_map, int64_t N, void* packed,
+                      int packed_dt, float* scales) {
     int64_t f;
 #pragma omp parallel for schedule(dynamic, 16)
     for (f = 0; f < N; ++f) {
@@ -279,7 +286,12 @@ static void copy_rows(const void* src, int src_dt, int64_t H, const int64_t* src
         if (row < 0)
             continue;
         int64_t s = src_row[f];
-        if (packed_dt == ORC_FP8) {
+        if (src_dt == ORC_FP8) {
+            memcpy((uint8_t*)packed + (size_t)row * H, (const uint8_t*)src + (size_t)s * H,
+                   (size_t)H);
+            memcpy(scales + row * (H / FP8_BLOCK), src_scales + s * (H / FP8_BLOCK),
+                   (size_t)(H / FP8_BLOCK) * sizeof(float));
+        } else if (packed_dt == ORC_FP8) {
             fp8_pack_row((const uint16_t*)src + s * H, H, (uint8_t*)packed + row * H,
                          scales + row * (H / FP8_BLOCK));
         } else {
@@ -294,10 +306,12 @@ static void copy_rows(const void* src, int src_dt, int64_t H, const int64_t* src
 /* dispatch ([mori#448] convert_dispatch_output)                        */
 /* ------------------------------------------------------------------ */
 
-int oracle_dispatch(const void* x, int x_dt, int64_t T, int64_t H, const int32_t* idx, int K,
-                    int E, int64_t cap, int64_t packed_rows, void* packed, int packed_dt,
-                    float* scales, int32_t* packed_cnt, int32_t* packed_off,
-                    int32_t* packed_src, int64_t* tok_map, int32_t* stats) {
+/* x_dt == ORC_FP8 is pre-quantized input: x holds e4m3 codes and x_scales the
+ * f32 scale of each 128-element block; both are forwarded unchanged. */
+int oracle_dispatch(const void* x, int x_dt, const float* x_scales, int64_t T, int64_t H,
+                    const int32_t* idx, int K, int E, int64_t cap, int64_t packed_rows,
+                    void* packed, int packed_dt, float* scales, int32_t* packed_cnt,
+                    int32_t* packed_off, int32_t* packed_src, int64_t* tok_map, int32_t* stats) {
     int64_t N = T * K, n_invalid = 0;
     uint8_t* keep = (uint8_t*)malloc((size_t)N + 1);
     int64_t* src_row = (int64_t*)malloc(((size_t)N + 1) * sizeof(int64_t));
@@ -310,13 +324,35 @@ int oracle_dispatch(const void* x, int x_dt, int64_t T, int64_t H, const int32_t
     }
     int64_t dropped = assign_slots(idx, keep, T, K, E, cap, packed_rows, packed_cnt, packed_off,
                                    packed_src, tok_map);
-    copy_rows(x, x_dt, H, src_row, tok_map, N, packed, packed_dt, scales);
+    copy_rows(x, x_dt, x_scales, H, src_row, tok_map, N, packed, packed_dt, scales);
     if (stats) {
         stats[0] = (int32_t)n_invalid;
         stats[1] = (int32_t)dropped;
         stats[2] = 0;
     }
     free(keep);
+    free(src_row);
+    return 0;
+}
+
+/* Replay dispatch (reading R-replay): the routing of an earlier dispatch is
+ * reused as it stands ([mori#448] commit "... replay dispatch (make_dispatch
+ * replay= reuses cached tok_map, identical layout)"), so only rows move: for
+ * every entry f with 0 <= tok_map[f] < packed_rows, packed[tok_map[f]] gets
+ * x[f / K] exactly as the dispatch would write it (bit copy, fp8 pack of bf16,
+ * or pre-quantized codes with their scale row).  Nothing else is written. */
+int oracle_dispatch_replay(const void* x, int x_dt, const float* x_scales, int64_t T, int64_t H,
+                           const int64_t* tok_map, int K, int64_t packed_rows, void* packed,
+                           int packed_dt, float* scales) {
+    int64_t N = T * K;
+    int64_t* rows = (int64_t*)malloc(((size_t)N + 1) * sizeof(int64_t));
+    int64_t* src_row = (int64_t*)malloc(((size_t)N + 1) * sizeof(int64_t));
+    for (int64_t f = 0; f < N; ++f) {
+        rows[f] = (tok_map[f] >= 0 && tok_map[f] < packed_rows) ? tok_map[f] : -1;
+        src_row[f] = f / K;
+    }
+    copy_rows(x, x_dt, x_scales, H, src_row, rows, N, packed, packed_dt, scales);
+    free(rows);
     free(src_row);
     return 0;
 }
@@ -493,7 +529,7 @@ int oracle_dedup_dispatch(const void* x, int x_dt, int64_t T, int64_t H, const i
     }
     entry_dropped += assign_slots(idx, keep, T, K, E, cap, packed_rows, packed_cnt, packed_off,
                                   packed_src, tok_map);
-    copy_rows(recv_x, x_dt, H, src_row, tok_map, N, packed, x_dt, NULL);
+    copy_rows(recv_x, x_dt, NULL, H, src_row, tok_map, N, packed, x_dt, NULL);
     if (stats) {
         stats[0] = (int32_t)n_invalid;
         stats[1] = (int32_t)entry_dropped;
