@@ -282,6 +282,69 @@ def measure(moe, W, name, args, dev, graphs=True, y_fp8=False):
     return r
 
 
+def dispatch_variants(moe, W, name, args, dev):
+    """The dispatch forms around the headline one, on the same fp8 workload:
+    replay along a cached tok_map (no routing), the pre-quantized dispatch (fp8
+    codes + scale rows forwarded, with routing) and its replay.  Median us of
+    args.steps timed calls after args.warmup, 3 rotating buffer sets."""
+    import numpy as np
+    import torch
+    d = W.make_inputs(name)
+    T, H, E, K = d["T"], d["H"], d["E"], d["K"]
+    stream = torch.cuda.current_stream(dev)
+    idx = torch.from_numpy(d["idx"]).to(dev)
+    x0 = torch.from_numpy(d["x"].view(np.int16)).view(torch.bfloat16).to(dev)
+    ws = moe.workspace(T, K, E, 0, dev)
+    sets = []
+    for _ in range(args.sets):
+        x = x0.clone()
+        o = moe.dispatch(x, idx, E, fp8=True, ws=ws)
+        xq = torch.empty((T, H), dtype=torch.uint8, device=dev)     # the token rows, pre-quantized
+        xs = torch.empty((T, H // 128), dtype=torch.float32, device=dev)
+        moe.dispatch_replay(x, torch.arange(T, dtype=torch.int64, device=dev).view(T, 1), xq, scales=xs)
+        sets.append(dict(x=x, o=o, xq=xq, xs=xs))
+    torch.cuda.synchronize()
+
+    def timeit(fn):
+        for i in range(args.warmup):
+            fn(sets[i % len(sets)])
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            ev[i][0].record(stream)
+            fn(sets[i % len(sets)])
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        us = [e[0].elapsed_time(e[1]) * 1e3 for e in ev]
+        return statistics.median(us[1:] if len(us) > 2 else us)
+
+    rows = T * K
+    meta = T * K * 8 + rows * 4 + E * 8
+    b_rep = T * H * 2 + rows * H + rows * (H // 128) * 4 + T * K * 8
+    b_pq = T * H + T * (H // 128) * 4 + rows * H + rows * (H // 128) * 4 + T * K * 4 + meta
+    b_pqr = T * H + T * (H // 128) * 4 + rows * H + rows * (H // 128) * 4 + T * K * 8
+    r_rep = timeit(lambda st: moe.dispatch_replay(st["x"], st["o"].tok_map, st["o"].packed,
+                                                  scales=st["o"].scales))
+    r_pq = timeit(lambda st: moe.dispatch_prequant(st["xq"], st["xs"], idx, E, out=st["o"], ws=ws))
+    r_pqr = timeit(lambda st: moe.dispatch_replay(st["xq"], st["o"].tok_map, st["o"].packed,
+                                                  scales=st["o"].scales, x_scales=st["xs"]))
+    # the replays and the pre-quantized dispatch reproduce the routed fp8 dispatch
+    st = sets[0]
+    ref = moe.dispatch(st["x"], idx, E, fp8=True, ws=ws)
+    pq = moe.dispatch_prequant(st["xq"], st["xs"], idx, E, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(pq.packed, ref.packed) and torch.equal(pq.tok_map, ref.tok_map)
+    del sets
+    torch.cuda.empty_cache()
+    gb = lambda b, us: round(b / (us * 1e-6) / 1e9, 1)
+    res = {"workload": name,
+           "replay_fp8_pack": {"us": round(r_rep, 2), "bytes": b_rep, "gbps": gb(b_rep, r_rep)},
+           "prequant_dispatch": {"us": round(r_pq, 2), "bytes": b_pq, "gbps": gb(b_pq, r_pq)},
+           "prequant_replay": {"us": round(r_pqr, 2), "bytes": b_pqr, "gbps": gb(b_pqr, r_pqr)}}
+    log(f"[bench] dispatch variants: replay+fp8 pack {r_rep:.1f} us, pre-quantized {r_pq:.1f} us, "
+        f"pre-quantized replay {r_pqr:.1f} us")
+    return res
+
+
 def copy_ceiling(moe, dev, reps=10):
     """GB/s (bytes read + written) of the library's 16-byte streaming copy of
     1 GiB, on the same stream as the kernels."""
@@ -391,6 +454,10 @@ def main():
         log(f"[bench] fp8-input combine: pair {s3['pair_us']:.1f} us, combine {s3['combine_us']:.1f} us "
             f"({f8['combine_gbps']:.0f} GB/s)")
 
+    dv = None
+    if r["fp8"] and not args.no_fp8_combine:
+        dv = dispatch_variants(moe, W, name, args, dev)
+
     copy_gbs = copy_ceiling(moe, dev)
     log(f"[bench] 16-byte streaming copy of 1 GiB: {copy_gbs:.0f} GB/s (read + write)")
 
@@ -436,6 +503,7 @@ def main():
                      "avg_launch_us": round(c_avg, 2)},
         "secondary": sec,
         "fp8_combine": f8,
+        "dispatch_variants": dv,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -6,10 +6,9 @@ binding.  Import is cheap: the library is loaded on first use and its absence
 raises instead of falling back to anything else.
 """
 from ._lib import (DedupOut, DedupPlan, DispatchOut, MoeError, combine, combine_fp8, copy16,
-                   dedup_dispatch,
-                   dispatch, fp8_dequant, load, route_count, version, workspace, workspace_size)
+                   dedup_dispatch, dispatch, dispatch_prequant, dispatch_replay, fp8_dequant,
+                   load, route_count, version, workspace, workspace_size)
 
 __all__ = ["DedupOut", "DedupPlan", "DispatchOut", "MoeError", "combine", "combine_fp8", "copy16",
-           "dedup_dispatch",
-           "dispatch", "fp8_dequant", "load", "route_count", "version", "workspace",
-           "workspace_size"]
+           "dedup_dispatch", "dispatch", "dispatch_prequant", "dispatch_replay", "fp8_dequant",
+           "load", "route_count", "version", "workspace", "workspace_size"]

@@ -68,8 +68,12 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.moe_fp8_dequant.argtypes = [_P, _P, _I64, _I64, _P, _P]
     lib.moe_copy16.argtypes = [_P, _P, _I64, _P]
     lib.moe_combine_fp8.argtypes = [_P, _P, _I64, _I64, _P, _P, _I64, _I32, _P, _I32, _P, _P]
+    lib.moe_dispatch_prequant.argtypes = [_P, _P, _I64, _I64, _P, _I32, _I32, _I64, _I64, _P, _P,
+                                          _P, _P, _P, _P, _P, _P, _SZ, _P]
+    lib.moe_dispatch_replay.argtypes = [_P, _I32, _P, _I64, _I64, _P, _I32, _I64, _P, _I32, _P, _P]
     for fn in ("moe_route_count", "moe_dispatch", "moe_combine", "moe_dedup_dispatch",
-               "moe_fp8_dequant", "moe_copy16", "moe_combine_fp8"):
+               "moe_fp8_dequant", "moe_copy16", "moe_combine_fp8", "moe_dispatch_prequant",
+               "moe_dispatch_replay"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -176,6 +180,43 @@ def dispatch(x: torch.Tensor, idx: torch.Tensor, E: int, cap: int = 0,
                                ptr(o.packed_off), ptr(o.packed_src), ptr(o.tok_map), ptr(o.stats),
                                ptr(ws), ws.numel(), _stream(dev)))
     return o
+
+
+def dispatch_prequant(x_q: torch.Tensor, x_scales: torch.Tensor, idx: torch.Tensor, E: int,
+                      cap: int = 0, packed_rows: Optional[int] = None,
+                      out: Optional[DispatchOut] = None, ws=None) -> DispatchOut:
+    """Dispatch of pre-quantized input: x_q uint8 [T,H] e4m3 codes, x_scales f32
+    [T,H/128]; codes and scale rows are forwarded unchanged."""
+    T, H = x_q.shape
+    K = idx.shape[1]
+    if packed_rows is None:
+        packed_rows = E * cap if cap > 0 else T * K
+    dev = x_q.device
+    o = alloc_dispatch(T, H, K, E, packed_rows, torch.uint8, True, dev) if out is None else out
+    ws = _ws(ws, T, K, E, 0, dev)
+    _check(load().moe_dispatch_prequant(ptr(x_q), ptr(x_scales), T, H, ptr(idx), K, E, cap,
+                                        packed_rows, ptr(o.packed), ptr(o.scales),
+                                        ptr(o.packed_cnt), ptr(o.packed_off), ptr(o.packed_src),
+                                        ptr(o.tok_map), ptr(o.stats), ptr(ws), ws.numel(),
+                                        _stream(dev)))
+    return o
+
+
+def dispatch_replay(x: torch.Tensor, tok_map: torch.Tensor, packed: torch.Tensor,
+                    scales: Optional[torch.Tensor] = None,
+                    x_scales: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Move the rows of x [T,H] into packed along a cached tok_map [T,K] (no
+    routing).  packed uint8 with x bf16 packs to fp8 (scales out); x uint8 with
+    x_scales is pre-quantized input."""
+    T, H = x.shape
+    K = tok_map.shape[1]
+    dev = x.device
+    x_dt = MOE_FP8_E4M3 if x.dtype == torch.uint8 else dtype_code(x.dtype)
+    pdt = MOE_FP8_E4M3 if packed.dtype == torch.uint8 else dtype_code(packed.dtype)
+    _check(load().moe_dispatch_replay(ptr(x), x_dt, ptr(x_scales), T, H, ptr(tok_map), K,
+                                      packed.shape[0], ptr(packed), pdt, ptr(scales),
+                                      _stream(dev)))
+    return packed
 
 
 def combine(y: torch.Tensor, tok_map: torch.Tensor, w: torch.Tensor, E: int = 0,

@@ -258,31 +258,67 @@ MOE_API int moe_route_count(const int32_t* idx, int64_t T, int K, int E, int32_t
     return ok();
 }
 
-MOE_API int moe_dispatch(const void* x, moe_dtype x_dt, int64_t T, int64_t H, const int32_t* idx,
-                         int K, int E, int64_t cap, int64_t packed_rows, void* packed_x,
-                         moe_dtype packed_dt, float* packed_scales, int32_t* packed_cnt,
-                         int32_t* packed_off, int32_t* packed_src, int64_t* tok_map,
-                         int32_t* stats, void* ws, size_t ws_bytes, void* stream) {
-    MOE_TRY(check_routing(T, K, E, idx));
-    if (x_dt != MOE_BF16 && x_dt != MOE_F32)
-        return fail(MOE_ERR_INVALID_ARG, "x dtype must be MOE_BF16 or MOE_F32");
-    const bool fp8 = packed_dt == MOE_FP8_E4M3;
-    if (packed_dt != x_dt && !fp8)
+namespace {
+
+// Payload checks shared by the dispatch entry points: bf16 -> bf16 or fp8
+// (pack), f32 -> f32, pre-quantized fp8 -> fp8 with its scale rows.
+int check_payload(const void* x, moe_dtype x_dt, const float* x_scales, int64_t T, int64_t H,
+                  int64_t packed_rows, const void* packed_x, moe_dtype packed_dt,
+                  const float* packed_scales) {
+    if (x_dt != MOE_BF16 && x_dt != MOE_F32 && x_dt != MOE_FP8_E4M3)
+        return fail(MOE_ERR_INVALID_ARG, "x dtype must be MOE_BF16, MOE_F32 or MOE_FP8_E4M3");
+    const bool fp8_out = packed_dt == MOE_FP8_E4M3;
+    if (packed_dt != x_dt && !fp8_out)
         return fail(MOE_ERR_INVALID_ARG, "packed dtype must equal x dtype or be MOE_FP8_E4M3");
-    if (fp8 && x_dt != MOE_BF16)
+    if (fp8_out && x_dt == MOE_F32)
         return fail(MOE_ERR_UNSUPPORTED, "fp8 packing is implemented for bf16 input only");
-    MOE_TRY(check_H(H, fp8));
-    if (cap < 0) return fail(MOE_ERR_INVALID_ARG, "cap must be >= 0");
+    MOE_TRY(check_H(H, fp8_out));
     if (packed_rows < 0 || packed_rows > kMaxRows)
         return fail(MOE_ERR_INVALID_ARG, "packed_rows must be in [0, 2^31-1]");
     MOE_TRY(check_rows_ptr(x, T, "x"));
     MOE_TRY(check_rows_ptr(packed_x, packed_rows, "packed_x"));
-    if (fp8 && packed_rows > 0 && !packed_scales)
+    if (fp8_out && packed_rows > 0 && !packed_scales)
         return fail(MOE_ERR_INVALID_ARG, "packed_scales is NULL for fp8");
-    if (!fp8 && packed_scales)
+    if (!fp8_out && packed_scales)
         return fail(MOE_ERR_INVALID_ARG, "packed_scales must be NULL unless fp8");
     if (packed_scales && !aligned(packed_scales, 4))
         return fail(MOE_ERR_INVALID_ARG, "packed_scales is not 4-byte aligned");
+    if (x_dt == MOE_FP8_E4M3 && T > 0 && !x_scales)
+        return fail(MOE_ERR_INVALID_ARG, "x_scales is NULL for pre-quantized input");
+    if (x_dt != MOE_FP8_E4M3 && x_scales)
+        return fail(MOE_ERR_INVALID_ARG, "x_scales must be NULL unless x is fp8");
+    if (x_scales && !aligned(x_scales, 4))
+        return fail(MOE_ERR_INVALID_ARG, "x_scales is not 4-byte aligned");
+    return MOE_OK;
+}
+
+moe::ScatterArgs scatter_args(const void* x, moe_dtype x_dt, const float* x_scales, int64_t T,
+                              int64_t H, moe_dtype packed_dt, void* packed_x, float* packed_scales,
+                              int32_t* packed_src, int64_t* tok_map) {
+    moe::ScatterArgs sa{};
+    sa.x = x;
+    sa.x_scales = x_dt == MOE_FP8_E4M3 ? x_scales : nullptr;
+    sa.T = T;
+    sa.H = H;
+    sa.x_bytes = elem_bytes(x_dt);
+    sa.fp8 = packed_dt == MOE_FP8_E4M3 && x_dt == MOE_BF16;
+    sa.replay = false;
+    sa.packed = packed_x;
+    sa.scales = packed_scales;
+    sa.packed_src = packed_src;
+    sa.tok_map = tok_map;
+    return sa;
+}
+
+int dispatch_impl(const void* x, moe_dtype x_dt, const float* x_scales, int64_t T, int64_t H,
+                  const int32_t* idx, int K, int E, int64_t cap, int64_t packed_rows,
+                  void* packed_x, moe_dtype packed_dt, float* packed_scales, int32_t* packed_cnt,
+                  int32_t* packed_off, int32_t* packed_src, int64_t* tok_map, int32_t* stats,
+                  void* ws, size_t ws_bytes, void* stream) {
+    MOE_TRY(check_routing(T, K, E, idx));
+    MOE_TRY(check_payload(x, x_dt, x_scales, T, H, packed_rows, packed_x, packed_dt,
+                          packed_scales));
+    if (cap < 0) return fail(MOE_ERR_INVALID_ARG, "cap must be >= 0");
     if (!packed_cnt) return fail(MOE_ERR_INVALID_ARG, "packed_cnt is NULL");
     if (packed_rows > 0 && !packed_src) return fail(MOE_ERR_INVALID_ARG, "packed_src is NULL");
     if (T > 0 && !tok_map) return fail(MOE_ERR_INVALID_ARG, "tok_map is NULL");
@@ -291,26 +327,65 @@ MOE_API int moe_dispatch(const void* x, moe_dtype x_dt, int64_t T, int64_t H, co
     MOE_TRY(check_ws(ws, ws_bytes, L.total));
     hipStream_t s = (hipStream_t)stream;
 
-    moe::ScatterArgs sa;
+    moe::ScatterArgs sa = scatter_args(x, x_dt, x_scales, T, H, packed_dt, packed_x,
+                                       packed_scales, packed_src, tok_map);
     sa.slot = slot_args(ws, L.experts, idx, K, E, cap, packed_rows);
-    sa.x = x;
-    sa.T = T;
-    sa.H = H;
-    sa.x_bytes = elem_bytes(x_dt);
-    sa.fp8 = fp8;
-    sa.packed = packed_x;
-    sa.scales = packed_scales;
-    sa.packed_src = packed_src;
-    sa.tok_map = tok_map;
 
     LevelOut o;
     o.packed_cnt = packed_cnt;
     o.packed_off = packed_off;
     o.stats = stats;
-    MOE_HIP(route_level(ws, L.experts, L.ticket, moe::KeyKind::Experts, idx, nullptr, T * K, K, E, 0, E, cap,
-                        packed_rows, o, moe::StatsMode::Plain, s),
-            "moe_dispatch routing");
-    MOE_HIP(moe::launch_scatter(sa, s), "moe_dispatch scatter");
+    MOE_HIP(route_level(ws, L.experts, L.ticket, moe::KeyKind::Experts, idx, nullptr, T * K, K, E,
+                        0, E, cap, packed_rows, o, moe::StatsMode::Plain, s),
+            "dispatch routing");
+    MOE_HIP(moe::launch_scatter(sa, s), "dispatch scatter");
+    return ok();
+}
+
+}  // namespace
+
+MOE_API int moe_dispatch(const void* x, moe_dtype x_dt, int64_t T, int64_t H, const int32_t* idx,
+                         int K, int E, int64_t cap, int64_t packed_rows, void* packed_x,
+                         moe_dtype packed_dt, float* packed_scales, int32_t* packed_cnt,
+                         int32_t* packed_off, int32_t* packed_src, int64_t* tok_map,
+                         int32_t* stats, void* ws, size_t ws_bytes, void* stream) {
+    if (x_dt == MOE_FP8_E4M3)
+        return fail(MOE_ERR_INVALID_ARG, "fp8 input carries scales: use moe_dispatch_prequant");
+    return dispatch_impl(x, x_dt, nullptr, T, H, idx, K, E, cap, packed_rows, packed_x, packed_dt,
+                         packed_scales, packed_cnt, packed_off, packed_src, tok_map, stats, ws,
+                         ws_bytes, stream);
+}
+
+MOE_API int moe_dispatch_prequant(const uint8_t* x_q, const float* x_scales, int64_t T, int64_t H,
+                                  const int32_t* idx, int K, int E, int64_t cap,
+                                  int64_t packed_rows, uint8_t* packed_x, float* packed_scales,
+                                  int32_t* packed_cnt, int32_t* packed_off, int32_t* packed_src,
+                                  int64_t* tok_map, int32_t* stats, void* ws, size_t ws_bytes,
+                                  void* stream) {
+    return dispatch_impl(x_q, MOE_FP8_E4M3, x_scales, T, H, idx, K, E, cap, packed_rows, packed_x,
+                         MOE_FP8_E4M3, packed_scales, packed_cnt, packed_off, packed_src, tok_map,
+                         stats, ws, ws_bytes, stream);
+}
+
+MOE_API int moe_dispatch_replay(const void* x, moe_dtype x_dt, const float* x_scales, int64_t T,
+                                int64_t H, const int64_t* tok_map, int K, int64_t packed_rows,
+                                void* packed_x, moe_dtype packed_dt, float* packed_scales,
+                                void* stream) {
+    if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T=%lld must be >= 0", (long long)T);
+    if (K < 1 || K > 16) return fail(MOE_ERR_INVALID_ARG, "K=%d must be in [1,16]", K);
+    if (T * (int64_t)K >= ((int64_t)1 << 31))
+        return fail(MOE_ERR_INVALID_ARG, "T*K=%lld must be < 2^31", (long long)(T * K));
+    MOE_TRY(check_payload(x, x_dt, x_scales, T, H, packed_rows, packed_x, packed_dt,
+                          packed_scales));
+    if (T > 0 && !tok_map) return fail(MOE_ERR_INVALID_ARG, "tok_map is NULL");
+    if (tok_map && !aligned(tok_map, 8)) return fail(MOE_ERR_INVALID_ARG, "tok_map is not 8-byte aligned");
+    moe::ScatterArgs sa = scatter_args(x, x_dt, x_scales, T, H, packed_dt, packed_x,
+                                       packed_scales, nullptr, const_cast<int64_t*>(tok_map));
+    sa.replay = true;
+    sa.slot = moe::SlotArgs{};
+    sa.slot.K = K;
+    sa.slot.packed_rows = packed_rows;
+    MOE_HIP(moe::launch_scatter(sa, (hipStream_t)stream), "moe_dispatch_replay");
     return ok();
 }
 

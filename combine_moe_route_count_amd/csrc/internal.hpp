@@ -65,13 +65,15 @@ struct SlotArgs {             // how an entry finds its packed row
 struct ScatterArgs {
     SlotArgs slot;
     const void* x;             // [T,H]
+    const float* x_scales;     // pre-quantized input: [T,H/128] forwarded to scales; else null
     int64_t T, H;
-    int x_bytes;               // 2 (bf16) or 4 (f32)
+    int x_bytes;               // 2 (bf16), 4 (f32) or 1 (pre-quantized e4m3)
     bool fp8;                  // pack bf16 -> e4m3 + scales
+    bool replay;               // rows from the cached tok_map; tok_map and packed_src not written
     void* packed;
     float* scales;
     int32_t* packed_src;
-    int64_t* tok_map;
+    int64_t* tok_map;          // written by the routed dispatch, read by the replay
 };
 hipError_t launch_scatter(const ScatterArgs& a, hipStream_t s);
 

@@ -26,11 +26,51 @@ constexpr int kCopyThreads = 256;
 // ---------------------------------------------------------------------------
 // plain dispatch, bit copy (bf16 or f32)
 // ---------------------------------------------------------------------------
-template <int DMAX, int VPT>
-__device__ __forceinline__ void scatter_copy_kernel_item(const ScatterArgs& a, int64_t t, int nth) {
+// Destination rows of token t, broadcast to every lane.  REPLAY: the rows of a
+// cached tok_map, taken as they stand when inside [0, packed_rows) (nothing is
+// written back); otherwise the routing lookup, which also writes tok_map and
+// packed_src.
+template <int DMAX, bool REPLAY>
+__device__ __forceinline__ void token_rows(const ScatterArgs& a, int64_t t, int (&rows)[DMAX]) {
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
     const int K = a.slot.K;
+    int my_row = -1;
+    if (REPLAY) {
+        if (lane < K) {
+            const int64_t r = a.tok_map[t * K + lane];
+            my_row = (r >= 0 && r < a.slot.packed_rows) ? (int)r : -1;
+        }
+    } else {
+        if (lane < K) my_row = entry_row(a.slot, t * K + lane);
+        if (tid < K) {
+            a.tok_map[t * K + tid] = my_row;
+            if (my_row >= 0) a.packed_src[my_row] = (int32_t)t;
+        }
+    }
+    broadcast_rows<DMAX>(my_row, rows);
+}
+
+// Pre-quantized input: the token's row of block scales goes unchanged to every
+// destination row.
+template <int DMAX>
+__device__ __forceinline__ void forward_scales(const ScatterArgs& a, int64_t t, const int (&rows)[DMAX],
+                                               int nth) {
+    const int64_t nblk = a.H / kFp8Block;
+    for (int64_t i = threadIdx.x; i < nblk; i += nth) {
+        float v = a.x_scales[t * nblk + i];
+        asm volatile("" : "+v"(v));   // one wait for the load, not one per conditional store
+#pragma unroll
+        for (int d = 0; d < DMAX; ++d) {
+            if (d >= a.slot.K) break;
+            if (rows[d] >= 0) a.scales[(int64_t)rows[d] * nblk + i] = v;
+        }
+    }
+}
+
+template <int DMAX, int VPT, bool REPLAY, bool SC>
+__device__ __forceinline__ void scatter_copy_kernel_item(const ScatterArgs& a, int64_t t, int nth) {
+    const int tid = threadIdx.x;
     const int64_t row_bytes = a.H * a.x_bytes;
     const int nvec = (int)(row_bytes / 16);
     const char* src = (const char*)a.x + t * row_bytes;
@@ -38,25 +78,21 @@ __device__ __forceinline__ void scatter_copy_kernel_item(const ScatterArgs& a, i
     u32x4 val[VPT];
     load_first_pass<VPT>(src, nvec, val, tid, nth);
 
-    int my_row = -1;
-    if (lane < K) my_row = entry_row(a.slot, t * K + lane);
-    if (tid < K) {
-        a.tok_map[t * K + tid] = my_row;
-        if (my_row >= 0) a.packed_src[my_row] = (int32_t)t;
-    }
     int rows[DMAX];
-    broadcast_rows<DMAX>(my_row, rows);
-    store_row_copies<DMAX, VPT>(src, nvec, (char*)a.packed, row_bytes, rows, K, val, tid, nth);
+    token_rows<DMAX, REPLAY>(a, t, rows);
+    // scales first: loading them after the row stores would reuse registers the
+    // stores still read, and the compiler would wait for every store first
+    if (SC) forward_scales<DMAX>(a, t, rows, nth);
+    store_row_copies<DMAX, VPT>(src, nvec, (char*)a.packed, row_bytes, rows, a.slot.K, val, tid, nth);
 }
 
 // ---------------------------------------------------------------------------
 // plain dispatch, fused blockwise fp8 pack (bf16 in)
 // ---------------------------------------------------------------------------
 
-template <int DMAX, int UPT>
+template <int DMAX, int UPT, bool REPLAY>
 __device__ __forceinline__ void scatter_fp8_kernel_item(const ScatterArgs& a, int64_t t, int nth) {
     const int tid = threadIdx.x;
-    const int lane = tid % kWave;
     const int K = a.slot.K;
     const int64_t H = a.H;
     const int nunits = (int)(H / 16);          // 16 elements per lane-unit
@@ -77,14 +113,8 @@ __device__ __forceinline__ void scatter_fp8_kernel_item(const ScatterArgs& a, in
         }
     }
 
-    int my_row = -1;
-    if (lane < K) my_row = entry_row(a.slot, t * K + lane);
-    if (tid < K) {
-        a.tok_map[t * K + tid] = my_row;
-        if (my_row >= 0) a.packed_src[my_row] = (int32_t)t;
-    }
     int rows[DMAX];
-    broadcast_rows<DMAX>(my_row, rows);
+    token_rows<DMAX, REPLAY>(a, t, rows);
     for (int base = 0;;) {
         u32x4 q[UPT];
         float s[UPT];
@@ -219,15 +249,15 @@ __device__ __forceinline__ void expand_kernel_item(const ExpandArgs& a, int64_t 
 // 16-bit field that gfx9 can only read with a vector load, which the compiler
 // repeats after every store it cannot prove disjoint and then waits for with
 // vmcnt(0), i.e. for every store in flight.
-template <int DMAX, int VPT>
+template <int DMAX, int VPT, bool REPLAY, bool SC>
 __global__ __launch_bounds__(kCopyThreads) void scatter_copy_kernel(ScatterArgs a, int nth) {
     for (int64_t t = blockIdx.x; t < a.T; t += gridDim.x)
-        scatter_copy_kernel_item<DMAX, VPT>(a, t, nth);
+        scatter_copy_kernel_item<DMAX, VPT, REPLAY, SC>(a, t, nth);
 }
-template <int DMAX, int UPT>
+template <int DMAX, int UPT, bool REPLAY>
 __global__ __launch_bounds__(kCopyThreads) void scatter_fp8_kernel(ScatterArgs a, int nth) {
     for (int64_t t = blockIdx.x; t < a.T; t += gridDim.x)
-        scatter_fp8_kernel_item<DMAX, UPT>(a, t, nth);
+        scatter_fp8_kernel_item<DMAX, UPT, REPLAY>(a, t, nth);
 }
 template <int DMAX, int VPT>
 __global__ __launch_bounds__(kCopyThreads) void recv_copy_kernel(RecvArgs a, int nth) {
@@ -321,17 +351,23 @@ hipError_t by_dmax(int D, dim3 grid, int threads, const Args& a, hipStream_t s) 
     return hipGetLastError();
 }
 
-template <int D, int V>
-struct LaunchCopy {
-    static void go(dim3 g, int th, const ScatterArgs& a, hipStream_t s) {
-        scatter_copy_kernel<D, V><<<g, dim3(th), 0, s>>>(a, th);
-    }
+template <bool REPLAY, bool SC>
+struct CopyMode {
+    template <int D, int V>
+    struct Launch {
+        static void go(dim3 g, int th, const ScatterArgs& a, hipStream_t s) {
+            scatter_copy_kernel<D, V, REPLAY, SC><<<g, dim3(th), 0, s>>>(a, th);
+        }
+    };
 };
-template <int D, int V>
-struct LaunchFp8 {
-    static void go(dim3 g, int th, const ScatterArgs& a, hipStream_t s) {
-        scatter_fp8_kernel<D, V><<<g, dim3(th), 0, s>>>(a, th);
-    }
+template <bool REPLAY>
+struct Fp8Mode {
+    template <int D, int V>
+    struct Launch {
+        static void go(dim3 g, int th, const ScatterArgs& a, hipStream_t s) {
+            scatter_fp8_kernel<D, V, REPLAY><<<g, dim3(th), 0, s>>>(a, th);
+        }
+    };
 };
 template <int D, int V>
 struct LaunchRecv {
@@ -354,11 +390,17 @@ hipError_t launch_scatter(const ScatterArgs& a, hipStream_t s) {
     if (a.fp8) {
         const int nunits = (int)(a.H / 16);
         const int th = copy_threads<2>(nunits);
-        return by_dmax<LaunchFp8, 2>(a.slot.K, grid, th, a, s);
+        return a.replay ? by_dmax<Fp8Mode<true>::Launch, 2>(a.slot.K, grid, th, a, s)
+                        : by_dmax<Fp8Mode<false>::Launch, 2>(a.slot.K, grid, th, a, s);
     }
     const int nvec = (int)(a.H * a.x_bytes / 16);
     const int th = copy_threads<4>(nvec);
-    return by_dmax<LaunchCopy, 4>(a.slot.K, grid, th, a, s);
+    const bool sc = a.x_scales != nullptr;
+    if (a.replay)
+        return sc ? by_dmax<CopyMode<true, true>::Launch, 4>(a.slot.K, grid, th, a, s)
+                  : by_dmax<CopyMode<true, false>::Launch, 4>(a.slot.K, grid, th, a, s);
+    return sc ? by_dmax<CopyMode<false, true>::Launch, 4>(a.slot.K, grid, th, a, s)
+              : by_dmax<CopyMode<false, false>::Launch, 4>(a.slot.K, grid, th, a, s);
 }
 
 hipError_t launch_recv_copy(const RecvArgs& a, hipStream_t s) {

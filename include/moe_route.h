@@ -121,6 +121,41 @@ int moe_dispatch(const void* x, moe_dtype x_dt, int64_t T, int64_t H, const int3
                  int32_t* packed_src, int64_t* tok_map, int32_t* stats, void* ws, size_t ws_bytes,
                  void* stream);
 
+/* Dispatch of pre-quantized input (the dispatch of "Draft: cco + flydsl
+ * dispatch/combine", commit "... routing handle, LEC, reset, replay", forwards
+ * the per-token quant scales with the payload): x_q holds e4m3fn codes and
+ * x_scales one f32 scale per 128-element block of each token; every packed row
+ * of token t receives x_q[t] byte for byte and its scale row receives
+ * x_scales[t] unchanged.  The routing outputs (tok_map, packed_*, stats) are
+ * those of moe_dispatch on the same ids.
+ *   x_q       uint8 [T,H], 16-byte aligned; H % 128 == 0
+ *   x_scales  f32 [T,H/128]
+ *   packed_x  uint8 [packed_rows,H]; packed_scales f32 [packed_rows,H/128]
+ *   the other arguments, limits and errors as for moe_dispatch. */
+int moe_dispatch_prequant(const uint8_t* x_q, const float* x_scales, int64_t T, int64_t H,
+                          const int32_t* idx, int K, int E, int64_t cap, int64_t packed_rows,
+                          uint8_t* packed_x, float* packed_scales, int32_t* packed_cnt,
+                          int32_t* packed_off, int32_t* packed_src, int64_t* tok_map,
+                          int32_t* stats, void* ws, size_t ws_bytes, void* stream);
+
+/* Replay dispatch (same page and commit: the replay reuses the cached tok_map
+ * with the identical layout): no counting, scan or slotting; for every entry
+ * with 0 <= tok_map[t,k] < packed_rows, row tok_map[t,k] of packed_x receives
+ * token t exactly as moe_dispatch (bf16/f32 bit copy, bf16 -> fp8 pack) or
+ * moe_dispatch_prequant (fp8 codes plus the scale row) would write it.
+ * Nothing else is written: packed_src, packed_cnt and the routing stay as the
+ * earlier dispatch left them.  tok_map must hold each row at most once (any
+ * dispatch's tok_map does); rows named twice get one of the writers.
+ *   x, x_dt, x_scales   payload as for moe_dispatch / moe_dispatch_prequant
+ *                       (x_scales only with x_dt == MOE_FP8_E4M3)
+ *   tok_map int64 [T,K], 8-byte aligned; K in [1,16]; T*K < 2^31
+ *   packed_x, packed_dt, packed_scales as for moe_dispatch.
+ * Errors: MOE_ERR_INVALID_ARG / MOE_ERR_UNSUPPORTED as for moe_dispatch; a
+ * failing call enqueues nothing.  Needs no workspace. */
+int moe_dispatch_replay(const void* x, moe_dtype x_dt, const float* x_scales, int64_t T, int64_t H,
+                        const int64_t* tok_map, int K, int64_t packed_rows, void* packed_x,
+                        moe_dtype packed_dt, float* packed_scales, void* stream);
+
 /* Dedup description for moe_combine: the routing outputs of moe_dedup_dispatch.
  *   idx        int32 [T,K] the ids the dispatch was given (for e / (E/R))
  *   rank_slot  int32 [T,R] recv row of (t, r) or -1

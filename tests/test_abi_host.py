@@ -126,6 +126,33 @@ res["combine_fp8"] = {
     "q_unaligned": c8(q=A8), "scales_unaligned": c8(sc=P(0x100002)), "tm_null": c8(tm=None),
     "out_unaligned": c8(out=A8), "Tneg": c8(T=-1), "y_rows_neg": c8(yr=-1),
 }
+def rp(**kw):
+    a = dict(x=A, xdt=0, xs=None, T=5, H=128, tm=A, K=2, rows=10, px=A, pdt=0, ps=None)
+    a.update(kw)
+    st = lib.moe_dispatch_replay(a["x"], a["xdt"], a["xs"], a["T"], a["H"], a["tm"], a["K"], a["rows"],
+                                 a["px"], a["pdt"], a["ps"], None)
+    return [st, lib.moe_last_error().decode()]
+
+def pq(**kw):
+    a = dict(x=A, xs=A, T=100, H=128, idx=A, K=4, E=16, cap=0, rows=400, px=A, ps=A, pc=A, po=None,
+             psrc=A, tm=A, st=None, ws=WS, wsb=ws_need)
+    a.update(kw)
+    st = lib.moe_dispatch_prequant(a["x"], a["xs"], a["T"], a["H"], a["idx"], a["K"], a["E"], a["cap"],
+                                   a["rows"], a["px"], a["ps"], a["pc"], a["po"], a["psrc"], a["tm"],
+                                   a["st"], a["ws"], a["wsb"], None)
+    return [st, lib.moe_last_error().decode()]
+
+res["replay"] = {
+    "K0": rp(K=0), "Tneg": rp(T=-1), "tm_null": rp(tm=None), "tm_unaligned": rp(tm=A4),
+    "dtype_mix": rp(pdt=1), "fp8_no_scales": rp(pdt=2), "f32_to_fp8": rp(xdt=1, pdt=2, ps=A),
+    "prequant_no_xscales": rp(xdt=2, pdt=2, ps=A), "xscales_not_fp8": rp(xs=A),
+    "fp8_H64": rp(pdt=2, ps=A, H=64), "x_unaligned": rp(x=A8), "rows_neg": rp(rows=-1),
+}
+res["prequant"] = {
+    "xs_null": pq(xs=None), "H64": pq(H=64), "ps_null": pq(ps=None), "K0": pq(K=0),
+    "ws_small": pq(wsb=ws_need - 1), "idx_null": pq(idx=None), "xs_unaligned": pq(xs=P(0x100002)),
+}
+res["dispatch"]["fp8_input"] = disp(x_dt=2, pdt=2, scales=A, H=128)
 res["route"] = {
     "cnt_null": [lib.moe_route_count(A, 10, 2, 4, None, A, None, WS, 1 << 20, None),
                  lib.moe_last_error().decode()],
@@ -197,6 +224,10 @@ def test_dedup_and_helpers_argument_errors():
         assert st == (WORKSPACE if case == "ws_small" else INVALID), (case, st, msg)
     for case, (st, msg) in _res()["dequant"].items():
         assert st == INVALID, (case, st, msg)
+    for case, (st, msg) in _res()["replay"].items():
+        assert st == (UNSUPPORTED if case == "f32_to_fp8" else INVALID) and msg, (case, st, msg)
+    for case, (st, msg) in _res()["prequant"].items():
+        assert st == (WORKSPACE if case == "ws_small" else INVALID) and msg, (case, st, msg)
     for case, (st, msg) in _res()["combine_fp8"].items():
         assert st == INVALID and msg, (case, st, msg)
     for case, (st, msg) in _res()["copy16"].items():

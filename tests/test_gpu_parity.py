@@ -534,3 +534,103 @@ def test_combine_fp8_skewed_full():
     assert _check_combine(host(out), exp, "bf16")
     np.testing.assert_array_equal(host(ow), ew)
 
+
+# ---------------------------------------------------------------------------
+# pre-quantized dispatch and replay dispatch
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("layout", ["compact", "padded", "padded_tight", "compact_short"])
+@pytest.mark.parametrize("T,K,E,H", [(300, 4, 13, 128), (2100, 8, 256, 384), (64, 2, 8, 7168)])
+def test_dispatch_prequant_small(layout, T, K, E, H):
+    rng = np.random.default_rng(T * 5 + K + H)
+    idx = _mixed_idx(rng, T, K, E)
+    q = rng.integers(0, 256, size=(T, H), dtype=np.uint8)
+    sc = (rng.random((T, H // 128)) + 0.5).astype(np.float32)
+    flat = idx.ravel()
+    cnt = np.bincount(flat[(flat >= 0) & (flat < E)], minlength=E)
+    cap = {"compact": 0, "padded": int(cnt.max()), "padded_tight": max(1, int(cnt.max()) // 2),
+           "compact_short": 0}[layout]
+    rows = {"compact": T * K, "padded": E * cap, "padded_tight": E * cap - 3,
+            "compact_short": max(0, int(cnt.sum()) - 37)}[layout]
+    note(f"dispatch_prequant {layout} T={T} K={K} E={E} H={H} cap={cap} rows={rows}")
+    o = moe._lib.alloc_dispatch(T, H, K, E, rows, torch.uint8, True, DEV)
+    for t in (o.packed, o.scales, o.packed_src, o.tok_map, o.packed_cnt, o.packed_off, o.stats):
+        poison_(t)
+    moe.dispatch_prequant(dev(q), dev(sc), dev(idx), E, cap=cap, packed_rows=rows, out=o)
+    torch.cuda.synchronize()
+    ref = oracle.dispatch(q, "fp8", idx, E, cap=cap, packed_rows=rows, x_scales=sc)
+    assert_dispatch_equal(o, ref, fp8=True)
+
+
+def test_dispatch_prequant_full():
+    d = W.make_inputs("skewed_fp8")
+    rng = np.random.default_rng(41)
+    q, sc = oracle.fp8_pack_rows(W.inject_outliers(d["x"], np.arange(0, d["T"], 97), 1000.0))
+    note("dispatch_prequant full T=8192")
+    o = moe._lib.alloc_dispatch(d["T"], d["H"], d["K"], d["E"], d["T"] * d["K"], torch.uint8, True, DEV)
+    for t in (o.packed, o.scales, o.packed_src, o.tok_map, o.packed_cnt, o.packed_off, o.stats):
+        poison_(t)
+    moe.dispatch_prequant(dev(q), dev(sc), dev(d["idx"]), d["E"], out=o)
+    torch.cuda.synchronize()
+    ref = oracle.dispatch(q, "fp8", d["idx"], d["E"], x_scales=sc)
+    assert_dispatch_equal(o, ref, fp8=True)
+
+
+def _replay_map(rng, T, K, rows, extra=8):
+    tm = rng.permutation(rows + extra)[:T * K].astype(np.int64).reshape(T, K)
+    tm[rng.random((T, K)) < 0.1] = -1
+    return tm
+
+
+@pytest.mark.parametrize("mode", ["bf16", "f32", "fp8_pack", "prequant"])
+@pytest.mark.parametrize("T,K,H", [(1, 1, 128), (300, 4, 256), (1500, 8, 7168)])
+def test_dispatch_replay_random_map(mode, T, K, H):
+    """A cached map with -1 entries and rows past packed_rows (skipped); rows
+    nobody names keep their poison."""
+    rng = np.random.default_rng(T + K + H)
+    rows = T * K + 5
+    tm = _replay_map(rng, T, K, rows)
+    xs = None
+    if mode == "prequant":
+        x = rng.integers(0, 256, size=(T, H), dtype=np.uint8)
+        xs = (rng.random((T, H // 128)) + 0.5).astype(np.float32)
+        x_dev, xdt, pdt = dev(x), "fp8", "fp8"
+    else:
+        xdt = "f32" if mode == "f32" else "bf16"
+        x = W.inject_outliers(W.normal_x(rng, T, H, xdt), np.arange(0, T, 11), 1000.0) if xdt == "bf16" else W.normal_x(rng, T, H, xdt)
+        x_dev = dev_x(x, xdt)
+        pdt = "fp8" if mode == "fp8_pack" else xdt
+    fp8 = pdt == "fp8"
+    pt = torch.uint8 if fp8 else x_dev.dtype
+    packed = torch.empty((rows, H), dtype=pt, device=DEV)
+    scales = torch.empty((rows, H // 128), dtype=torch.float32, device=DEV) if fp8 else None
+    poison_(packed)
+    poison_(scales)
+    note(f"dispatch_replay {mode} T={T} K={K} H={H}")
+    moe.dispatch_replay(x_dev, dev(tm), packed, scales=scales, x_scales=dev(xs) if xs is not None else None)
+    torch.cuda.synchronize()
+    ref = oracle.dispatch_replay(x, xdt, tm, rows, packed_dt=pdt, x_scales=xs)
+    np.testing.assert_array_equal(host(packed).view(np.uint8), ref["packed"].view(np.uint8))
+    if fp8:
+        np.testing.assert_array_equal(host(scales).view(np.uint32), ref["scales"].view(np.uint32))
+
+
+def test_dispatch_replay_equals_routed_dispatch():
+    """Replaying the metric workload's own tok_map reproduces the routed
+    dispatch's packed rows and scales bitwise, with new token rows each time."""
+    d = W.make_inputs("skewed_fp8")
+    E = d["E"]
+    note("dispatch_replay after routed dispatch, T=8192 fp8")
+    o = gpu_dispatch(dev_bf16(d["x"]), d["idx"], E, fp8=True)
+    x2 = W.inject_outliers(W.normal_x(np.random.default_rng(5), d["T"], d["H"], "bf16"),
+                           np.arange(0, d["T"], 13), 1000.0)
+    packed = torch.empty_like(o.packed)
+    scales = torch.empty_like(o.scales)
+    poison_(packed)
+    poison_(scales)
+    moe.dispatch_replay(dev_bf16(x2), o.tok_map, packed, scales=scales)
+    o2 = gpu_dispatch(dev_bf16(x2), d["idx"], E, fp8=True)
+    torch.cuda.synchronize()
+    assert torch.equal(packed, o2.packed)
+    assert torch.equal(scales.view(torch.int32), o2.scales.view(torch.int32))
+
