@@ -20,9 +20,18 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "moe_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
-BF16, F32, FP8 = 0, 1, 2
-DT = {"bf16": BF16, "f32": F32, "fp8": FP8}
-NP_DT = {BF16: np.uint16, F32: np.float32, FP8: np.uint8}
+BF16, F32, FP8, FP4 = 0, 1, 2, 3
+DT = {"bf16": BF16, "f32": F32, "fp8": FP8, "fp4": FP4}
+NP_DT = {BF16: np.uint16, F32: np.float32, FP8: np.uint8, FP4: np.uint8}
+
+
+def _row_width(dt, H):
+    """Array width of one packed row of H elements (fp4: two codes per byte)."""
+    return {BF16: H, F32: H, FP8: H, FP4: H // 2}[dt]
+
+
+def _quantized(dt):
+    return dt in (FP8, FP4)
 
 # Poison written into outputs before a call, so a row or slot that a call does
 # not own can be told apart from one it wrote.
@@ -56,6 +65,10 @@ def _load():
         "oracle_dispatch_replay": [P, I32, P, I64, I64, P, I32, I64, P, I32, P],
         "oracle_combine": [P, I32, I64, I64, P, P, I64, I32, P, I32, P],
         "oracle_combine_fp8": [P, P, I64, I64, P, P, I64, I32, P, I32, P],
+        "oracle_combine_fp4": [P, P, I64, I64, P, P, I64, I32, P, I32, P],
+        "oracle_e2m1_encode": [P, I64, P],
+        "oracle_e2m1_decode": [P, I64, P],
+        "oracle_fp4_pack_rows": [P, I64, I64, P, P],
         "oracle_dedup_dispatch": [P, I32, I64, I64, P, I32, I32, I32, P, I64, P, P, P, P, I64,
                                   I64, P, P, P, P, P, P],
         "oracle_dedup_combine": [P, I32, I64, I64, P, P, P, I64, I32, I32, I32, P, I64, P, P,
@@ -125,17 +138,18 @@ def dispatch(x: np.ndarray, x_dt: str, idx: np.ndarray, E: int, cap: int = 0,
     T, K = idx.shape
     xd = DT[x_dt]
     pd = DT[packed_dt or x_dt]
-    if pd != xd and not (pd == FP8 and xd == BF16):
-        raise ValueError("packed dtype must equal x dtype, or be fp8 from bf16")
+    if pd != xd and not (_quantized(pd) and xd == BF16):
+        raise ValueError("packed dtype must equal x dtype, or be fp8/fp4 from bf16")
     if (xd == FP8) != (x_scales is not None):
         raise ValueError("x_scales go with fp8 input, and only with it")
     xs = None if x_scales is None else _c(x_scales, np.float32)
     x = _c(x, NP_DT[xd])
     H = x.shape[1]
     rows = _rows_needed(idx, E, cap) if packed_rows is None else int(packed_rows)
-    eb = {BF16: 2, F32: 4, FP8: 1}[pd]
-    packed = np.full((rows, H * eb), POISON_BYTE, np.uint8).view(NP_DT[pd])
-    scales = np.full((rows, H // 128 * 4), POISON_BYTE, np.uint8).view(np.float32) if pd == FP8 else None
+    packed = np.full((rows, _row_width(pd, H)), POISON_BYTE, np.uint8).view(NP_DT[pd]) \
+        if pd in (FP8, FP4) else \
+        np.full((rows, H * (2 if pd == BF16 else 4)), POISON_BYTE, np.uint8).view(NP_DT[pd])
+    scales = np.full((rows, H // 128 * 4), POISON_BYTE, np.uint8).view(np.float32) if _quantized(pd) else None
     packed_cnt = np.empty(E, np.int32)
     packed_off = np.empty(E + 1, np.int32)
     packed_src = np.full(rows, POISON_I32, np.int32)
@@ -156,17 +170,18 @@ def dispatch_replay(x: np.ndarray, x_dt: str, tok_map: np.ndarray, packed_rows: 
     T, K = tok_map.shape
     xd = DT[x_dt]
     pd = DT[packed_dt or x_dt]
-    if pd != xd and not (pd == FP8 and xd == BF16):
-        raise ValueError("packed dtype must equal x dtype, or be fp8 from bf16")
+    if pd != xd and not (_quantized(pd) and xd == BF16):
+        raise ValueError("packed dtype must equal x dtype, or be fp8/fp4 from bf16")
     if (xd == FP8) != (x_scales is not None):
         raise ValueError("x_scales go with fp8 input, and only with it")
     xs = None if x_scales is None else _c(x_scales, np.float32)
     x = _c(x, NP_DT[xd])
     H = x.shape[1]
     rows = int(packed_rows)
-    eb = {BF16: 2, F32: 4, FP8: 1}[pd]
-    packed = np.full((rows, H * eb), POISON_BYTE, np.uint8).view(NP_DT[pd])
-    scales = np.full((rows, H // 128 * 4), POISON_BYTE, np.uint8).view(np.float32) if pd == FP8 else None
+    packed = np.full((rows, _row_width(pd, H)), POISON_BYTE, np.uint8).view(NP_DT[pd]) \
+        if pd in (FP8, FP4) else \
+        np.full((rows, H * (2 if pd == BF16 else 4)), POISON_BYTE, np.uint8).view(NP_DT[pd])
+    scales = np.full((rows, H // 128 * 4), POISON_BYTE, np.uint8).view(np.float32) if _quantized(pd) else None
     _load().oracle_dispatch_replay(_p(x), xd, _p(xs), T, H, _p(tok_map), K, rows, _p(packed), pd,
                                    _p(scales))
     return dict(packed=packed, scales=scales)
@@ -202,6 +217,50 @@ def combine_fp8(q: np.ndarray, scales, tok_map: np.ndarray, w: np.ndarray, out_d
     _load().oracle_combine_fp8(_p(q), _p(sc), y_rows, H, _p(tok_map), _p(w), T, K, _p(out), od,
                                _p(ow))
     return out, ow
+
+
+def combine_fp4(q: np.ndarray, scales, tok_map: np.ndarray, w: np.ndarray, out_dt: str):
+    """Combine of fp4 expert outputs: q uint8 [rows,H/2] (two e2m1 codes per byte,
+    element 2i in the low nibble), scales f32 [rows,H/128] or None."""
+    od = DT[out_dt]
+    q = _c(q, np.uint8)
+    sc = None if scales is None else _c(scales, np.float32)
+    tok_map = _c(tok_map, np.int64)
+    w = _c(w, np.float32)
+    T, K = tok_map.shape
+    y_rows, Hh = q.shape
+    H = 2 * Hh
+    assert H % 128 == 0 and (sc is None or sc.shape == (y_rows, H // 128))
+    out = np.empty((T, H), NP_DT[od])
+    ow = np.empty(T, np.float32)
+    _load().oracle_combine_fp4(_p(q), _p(sc), y_rows, H, _p(tok_map), _p(w), T, K, _p(out), od,
+                               _p(ow))
+    return out, ow
+
+
+def e2m1_encode(v: np.ndarray) -> np.ndarray:
+    """Encode values to e2m1 codes (0..15), round to nearest even, saturating at 6."""
+    v = _c(v, np.float32)
+    out = np.empty(v.shape, np.uint8)
+    _load().oracle_e2m1_encode(_p(v), v.size, _p(out))
+    return out
+
+
+def e2m1_decode(c: np.ndarray) -> np.ndarray:
+    c = _c(c, np.uint8)
+    out = np.empty(c.shape, np.float32)
+    _load().oracle_e2m1_decode(_p(c), c.size, _p(out))
+    return out
+
+
+def fp4_pack_rows(x_bf16: np.ndarray):
+    """Blockwise fp4 pack of bf16 rows: (q uint8 [rows,H/2], s f32 [rows,H/128])."""
+    x = _c(x_bf16, np.uint16)
+    rows, H = x.shape
+    q = np.empty((rows, H // 2), np.uint8)
+    s = np.empty((rows, H // 128), np.float32)
+    _load().oracle_fp4_pack_rows(_p(x), rows, H, _p(q), _p(s))
+    return q, s
 
 
 def dedup_dispatch(x: np.ndarray, x_dt: str, idx: np.ndarray, E: int, R: int,

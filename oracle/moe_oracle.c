@@ -48,6 +48,11 @@
  *   R-comb8  fp8 expert outputs: v = f32(e4m3(q)) * s with the block's f32
  *            scale (1 when no scales are given), one rounded multiply and no
  *            bf16 step, then the R-comb reduction over v.
+ *   R-fp4    fp4 payload: OCP e2m1 (max 6), round to nearest even, two codes
+ *            per byte with element 2i in the low nibble; the R-fp8 block rule
+ *            with 6 in place of 448 (s = amax/6 when amax > 6, else 1).
+ *   R-comb4  fp4 expert outputs: v = f32(e2m1(q)) * s, then the R-comb
+ *            reduction, as R-comb8.
  *   R-prequant  fp8 input (e4m3 codes with one f32 scale per 128-element
  *            block) is dispatched byte for byte and each token's scale row is
  *            forwarded unchanged to every packed row of the token.
@@ -79,7 +84,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORC_BF16 = 0, ORC_F32 = 1, ORC_FP8 = 2 };
+enum { ORC_BF16 = 0, ORC_F32 = 1, ORC_FP8 = 2, ORC_FP4 = 3 };
 
 /* ------------------------------------------------------------------ */
 /* number formats                                                       */
@@ -146,6 +151,34 @@ static uint8_t f32_to_e4m3(float v) {
     return (uint8_t)(sign | (uint8_t)(((E + 7) << 3) | (int)q));
 }
 
+/* OCP e2m1 (fp4): 1 sign bit, 2 exponent bits (bias 1), 1 mantissa bit.
+ * Exponent field 0: subnormal m * 0.5.  Fields 1..3: (1 + m/2) * 2^(E-1).
+ * Magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6; no infinities, no NaN. */
+static float e2m1_to_f32(uint8_t n) {
+    int E = (n >> 1) & 3, m = n & 1;
+    double v = E == 0 ? 0.5 * m : ldexp(1.0 + m / 2.0, E - 1);
+    return (float)((n & 8) ? -v : v);
+}
+
+/* Encode to e2m1, round to nearest, ties to the even code (mantissa bit 0);
+ * magnitudes above 6 saturate to 6; the sign is kept for zero results. */
+static uint8_t f32_to_e2m1(float v) {
+    uint8_t sign = signbit(v) ? 8 : 0;
+    double a = fabs((double)v);
+    uint8_t best = 0;
+    double bd = a;                              /* distance to code 0 */
+    for (uint8_t c = 1; c < 8; ++c) {
+        double d = fabs(a - (double)e2m1_to_f32(c));
+        if (d < bd || (d == bd && (c & 1) == 0)) {
+            bd = d;
+            best = c;
+        }
+    }
+    if (a > 6.0)
+        best = 7;
+    return sign | best;
+}
+
 static float load_elem(const void* base, int dt, int64_t i) {
     if (dt == ORC_BF16)
         return bf16_to_f32(((const uint16_t*)base)[i]);
@@ -184,6 +217,41 @@ static void fp8_pack_row(const uint16_t* xrow, int64_t H, uint8_t* q, float* s) 
             for (int h = 0; h < FP8_BLOCK; ++h)
                 q[b * FP8_BLOCK + h] = f32_to_e4m3(bf16_to_f32(xb[h]));
         }
+    }
+}
+
+/* fp4 blockwise pack of one row (reading R-fp4): the R-fp8 rule with the e2m1
+ * maximum 6.  Per 128-element block: amax = max|x|; amax > 6 gives s = amax/6
+ * and q = e2m1(clamp((x*6)/amax, +-6)) (x*6 is exact for bf16 x); otherwise
+ * s = 1 and q = e2m1(x).  Element 2i goes to the low nibble of byte i. */
+#define E2M1_MAX 6.0f
+
+static void fp4_pack_row(const uint16_t* xrow, int64_t H, uint8_t* q, float* s) {
+    for (int64_t b = 0; b * FP8_BLOCK < H; ++b) {
+        const uint16_t* xb = xrow + b * FP8_BLOCK;
+        float amax = 0.0f;
+        for (int h = 0; h < FP8_BLOCK; ++h) {
+            float a = fabsf(bf16_to_f32(xb[h]));
+            if (a > amax)
+                amax = a;
+        }
+        uint8_t codes[FP8_BLOCK];
+        if (amax > E2M1_MAX) {
+            s[b] = amax / E2M1_MAX;
+            for (int h = 0; h < FP8_BLOCK; ++h) {
+                float v = bf16_to_f32(xb[h]) * E2M1_MAX;
+                v = v / amax;
+                if (v > E2M1_MAX) v = E2M1_MAX;
+                if (v < -E2M1_MAX) v = -E2M1_MAX;
+                codes[h] = f32_to_e2m1(v);
+            }
+        } else {
+            s[b] = 1.0f;
+            for (int h = 0; h < FP8_BLOCK; ++h)
+                codes[h] = f32_to_e2m1(bf16_to_f32(xb[h]));
+        }
+        for (int h = 0; h < FP8_BLOCK; h += 2)
+            q[(b * FP8_BLOCK + h) / 2] = (uint8_t)(codes[h] | (codes[h + 1] << 4));
     }
 }
 
@@ -293,6 +361,9 @@ static void copy_rows(const void* src, int src_dt, const float* src_scales, int6
                    (size_t)(H / FP8_BLOCK) * sizeof(float));
         } else if (packed_dt == ORC_FP8) {
             fp8_pack_row((const uint16_t*)src + s * H, H, (uint8_t*)packed + row * H,
+                         scales + row * (H / FP8_BLOCK));
+        } else if (packed_dt == ORC_FP4) {
+            fp4_pack_row((const uint16_t*)src + s * H, H, (uint8_t*)packed + row * (H / 2),
                          scales + row * (H / FP8_BLOCK));
         } else {
             size_t eb = elem_bytes(src_dt);
@@ -425,6 +496,49 @@ int oracle_combine_fp8(const uint8_t* q, const float* scales, int64_t y_rows, in
             for (int64_t h = 0; h < H; ++h) {
                 float s = scales ? scales[row * nblk + h / FP8_BLOCK] : 1.0f;
                 float v = e4m3_to_f32(q[row * H + h]) * s;
+                float p = wk * v;
+                acc[h] = acc[h] + p;
+            }
+            ws = ws + wk;
+        }
+        for (int64_t h = 0; h < H; ++h) {
+            if (out_dt == ORC_BF16)
+                ((uint16_t*)out)[t * H + h] = f32_to_bf16(acc[h]);
+            else
+                ((float*)out)[t * H + h] = acc[h];
+        }
+        if (out_weights)
+            out_weights[t] = ws;
+        free(acc);
+    }
+    return 0;
+}
+
+/* Combine of fp4 expert outputs (reading R-comb4): as oracle_combine_fp8 with
+ * e2m1 codes, two per byte (element 2i in the low nibble), rows of H/2 bytes
+ * ([mori#448] commit "Add the fp4 e2m1 accum path ...": packed fp4 expanded to
+ * f32 with the scale, accumulated in f32). */
+int oracle_combine_fp4(const uint8_t* q, const float* scales, int64_t y_rows, int64_t H,
+                       const int64_t* tok_map, const float* w, int64_t T, int K, void* out,
+                       int out_dt, float* out_weights) {
+    const int64_t nblk = H / FP8_BLOCK;
+    int64_t t;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (t = 0; t < T; ++t) {
+        float* acc = (float*)malloc((size_t)H * sizeof(float));
+        float ws = 0.0f;
+        for (int64_t h = 0; h < H; ++h)
+            acc[h] = 0.0f;
+        for (int k = 0; k < K; ++k) {
+            int64_t row = tok_map[t * K + k];
+            if (row < 0 || row >= y_rows)
+                continue;
+            float wk = w[t * K + k];
+            for (int64_t h = 0; h < H; ++h) {
+                uint8_t byte = q[row * (H / 2) + h / 2];
+                uint8_t code = (h & 1) ? (byte >> 4) : (byte & 15);
+                float s = scales ? scales[row * nblk + h / FP8_BLOCK] : 1.0f;
+                float v = e2m1_to_f32(code) * s;
                 float p = wk * v;
                 acc[h] = acc[h] + p;
             }
@@ -634,6 +748,21 @@ int oracle_expert_scale(const uint16_t* packed, int64_t H, int E, const int32_t*
             for (int64_t h = 0; h < H; ++h)
                 y[row * H + h] = f32_to_bf16(c[e] * bf16_to_f32(packed[row * H + h]));
     return 0;
+}
+
+void oracle_e2m1_encode(const float* v, int64_t n, uint8_t* out) {
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = f32_to_e2m1(v[i]);
+}
+
+void oracle_e2m1_decode(const uint8_t* c, int64_t n, float* out) {
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = e2m1_to_f32(c[i] & 15);
+}
+
+void oracle_fp4_pack_rows(const uint16_t* x, int64_t rows, int64_t H, uint8_t* q, float* s) {
+    for (int64_t r = 0; r < rows; ++r)
+        fp4_pack_row(x + r * H, H, q + r * (H / 2), s + r * (H / FP8_BLOCK));
 }
 
 void oracle_bf16_encode(const float* v, int64_t n, uint16_t* out) {
