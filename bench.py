@@ -35,20 +35,22 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(T, H, K, E, N_rows, fp8=True, y_bytes=2, out_bytes=2, y_fp8=False):
+def algorithmic_bytes(T, H, K, E, N_rows, fp8=True, y_bytes=2, out_bytes=2, y_fp8=False, fp4=False):
     """Bytes the method must move per call (metadata once, rows once).  y_fp8:
-    the combine reads e4m3 expert outputs with one f32 scale per 128 elements."""
+    the combine reads the quantized expert outputs (one f32 scale per 128
+    elements); fp4: the payload is e2m1, two codes per byte."""
     idx = T * K * 4
     tok_map = T * K * 8
     w = T * K * 4
     x = T * H * 2
+    qrow = H // 2 if fp4 else H
     if fp8:
-        rows_w = N_rows * H + N_rows * (H // 128) * 4
+        rows_w = N_rows * qrow + N_rows * (H // 128) * 4
     else:
         rows_w = N_rows * H * 2
     meta_d = idx + tok_map + N_rows * 4 + E * 4 * 2   # idx in, tok_map/packed_src/cnt/off out
     disp = x + rows_w + meta_d
-    comb_rows = N_rows * H + N_rows * (H // 128) * 4 if y_fp8 else N_rows * H * y_bytes
+    comb_rows = N_rows * qrow + N_rows * (H // 128) * 4 if y_fp8 else N_rows * H * y_bytes
     comb = comb_rows + T * H * out_bytes + tok_map + w + T * 4
     return disp, comb
 
@@ -157,12 +159,13 @@ def cpu_baseline(name, T_full, sample_T):
                       f"{T_full}/{sample_T} to one full call; expert step excluded"}
 
 
-def measure(moe, W, name, args, dev, graphs=True, y_fp8=False):
+def measure(moe, W, name, args, dev, graphs=True, y_fp8=False, fp4=False):
     """Time dispatch+combine pairs of one workload; returns medians and spreads.
 
     Pass 1 (the headline): HIP events on the launch stream around each
     dispatch+combine pair, none between the two calls.  y_fp8: the combine takes
-    the fp8 packed rows and scales themselves (moe_combine_fp8, identity expert).  Pass 2 (breakdown): a
+    the fp8 packed rows and scales themselves (moe_combine_fp8, identity expert);
+    fp4 (with y_fp8): an e2m1 payload end to end (moe_combine_fp4).  Pass 2 (breakdown): a
     marker between dispatch and combine as well.  Pass 3: each pair replayed
     from a captured HIP graph, its outputs checked against the eager ones."""
     import numpy as np
@@ -180,7 +183,7 @@ def measure(moe, W, name, args, dev, graphs=True, y_fp8=False):
     sets = []
     for s_ in range(args.sets):
         x = x0.clone()
-        o = moe.dispatch(x, idx, E, fp8=fp8, ws=ws)
+        o = moe.dispatch(x, idx, E, fp8=fp8 and not fp4, ws=ws, fp4=fp4)
         if y_fp8:
             y = None
         else:
@@ -196,12 +199,12 @@ def measure(moe, W, name, args, dev, graphs=True, y_fp8=False):
         st = sets[i % len(sets)]
         if events is not None:
             events[0].record(stream)
-        moe.dispatch(st["x"], idx, E, fp8=fp8, out=st["o"], ws=ws)
+        moe.dispatch(st["x"], idx, E, fp8=fp8 and not fp4, out=st["o"], ws=ws, fp4=fp4)
         if events is not None and len(events) == 3:
             events[1].record(stream)
         if y_fp8:
-            moe.combine_fp8(st["o"].packed, st["o"].scales, st["o"].tok_map, w, out=st["out"],
-                            out_weights=st["ow"])
+            qc = moe.combine_fp4 if fp4 else moe.combine_fp8
+            qc(st["o"].packed, st["o"].scales, st["o"].tok_map, w, out=st["out"], out_weights=st["ow"])
         else:
             moe.combine(st["y"], st["o"].tok_map, w, out=st["out"], out_weights=st["ow"])
         if events is not None:
@@ -266,7 +269,7 @@ def measure(moe, W, name, args, dev, graphs=True, y_fp8=False):
 
     # drop the first timed round (start transient)
     tail = lambda v: v[1:] if len(v) > 2 else v
-    disp_b, comb_b = algorithmic_bytes(T, H, K, E, T * K, fp8=fp8, y_fp8=y_fp8)
+    disp_b, comb_b = algorithmic_bytes(T, H, K, E, T * K, fp8=fp8, y_fp8=y_fp8, fp4=fp4)
     r = dict(name=name, T=T, H=H, E=E, K=K, fp8=fp8, routing=d["workload"].routing,
              pair_us=statistics.median(tail(pair_us)), pair_us_min=min(tail(pair_us)),
              pair_us_std=statistics.pstdev(tail(pair_us)),
@@ -454,6 +457,20 @@ def main():
         log(f"[bench] fp8-input combine: pair {s3['pair_us']:.1f} us, combine {s3['combine_us']:.1f} us "
             f"({f8['combine_gbps']:.0f} GB/s)")
 
+    f4 = None
+    if r["fp8"] and not args.no_fp8_combine:
+        s4 = measure(moe, W, name, args, dev, graphs=False, y_fp8=True, fp4=True)
+        tb4 = s4["disp_b"] + s4["comb_b"]
+        g4 = tb4 / (s4["pair_us"] * 1e-6) / 1e9
+        f4 = {"workload": name, "payload": "fp4_e2m1+f32_scale_per_128",
+              "combine": "fp4_e2m1+f32_scale_per_128_in_f32_acc_bf16_out",
+              "pair_us": round(s4["pair_us"], 2), "pair_us_min": round(s4["pair_us_min"], 2),
+              "dispatch_us": round(s4["dispatch_us"], 2), "combine_us": round(s4["combine_us"], 2),
+              "algorithmic_bytes": {"dispatch": s4["disp_b"], "combine": s4["comb_b"]},
+              "achieved_gbps": round(g4, 1), "pct_hbm_peak": round(100 * g4 / HBM_PEAK_GBS, 2)}
+        log(f"[bench] fp4 payload: pair {s4['pair_us']:.1f} us (dispatch {s4['dispatch_us']:.1f}, "
+            f"combine {s4['combine_us']:.1f})")
+
     dv = None
     if r["fp8"] and not args.no_fp8_combine:
         dv = dispatch_variants(moe, W, name, args, dev)
@@ -503,6 +520,7 @@ def main():
                      "avg_launch_us": round(c_avg, 2)},
         "secondary": sec,
         "fp8_combine": f8,
+        "fp4_payload": f4,
         "dispatch_variants": dv,
         "cpu_baseline": cpu,
     }

@@ -5,10 +5,12 @@ C ABI, declared in include/moe_route.h); this package is its thin Python
 binding.  Import is cheap: the library is loaded on first use and its absence
 raises instead of falling back to anything else.
 """
-from ._lib import (DedupOut, DedupPlan, DispatchOut, MoeError, combine, combine_fp8, copy16,
+from ._lib import (DedupOut, DedupPlan, DispatchOut, MoeError, combine, combine_fp4, combine_fp8,
+                   copy16,
                    dedup_dispatch, dispatch, dispatch_prequant, dispatch_replay, fp8_dequant,
                    load, route_count, version, workspace, workspace_size)
 
-__all__ = ["DedupOut", "DedupPlan", "DispatchOut", "MoeError", "combine", "combine_fp8", "copy16",
+__all__ = ["DedupOut", "DedupPlan", "DispatchOut", "MoeError", "combine", "combine_fp4",
+           "combine_fp8", "copy16",
            "dedup_dispatch", "dispatch", "dispatch_prequant", "dispatch_replay", "fp8_dequant",
            "load", "route_count", "version", "workspace", "workspace_size"]

@@ -17,7 +17,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_route.so")
 
-MOE_BF16, MOE_F32, MOE_FP8_E4M3 = 0, 1, 2
+MOE_BF16, MOE_F32, MOE_FP8_E4M3, MOE_FP4_E2M1 = 0, 1, 2, 3
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 
 _P = ctypes.c_void_p
@@ -71,9 +71,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.moe_dispatch_prequant.argtypes = [_P, _P, _I64, _I64, _P, _I32, _I32, _I64, _I64, _P, _P,
                                           _P, _P, _P, _P, _P, _P, _SZ, _P]
     lib.moe_dispatch_replay.argtypes = [_P, _I32, _P, _I64, _I64, _P, _I32, _I64, _P, _I32, _P, _P]
+    lib.moe_combine_fp4.argtypes = [_P, _P, _I64, _I64, _P, _P, _I64, _I32, _P, _I32, _P, _P]
     for fn in ("moe_route_count", "moe_dispatch", "moe_combine", "moe_dedup_dispatch",
                "moe_fp8_dequant", "moe_copy16", "moe_combine_fp8", "moe_dispatch_prequant",
-               "moe_dispatch_replay"):
+               "moe_dispatch_replay", "moe_combine_fp4"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -150,11 +151,13 @@ class DispatchOut:
     stats: torch.Tensor
 
 
-def alloc_dispatch(T, H, K, E, packed_rows, x_dtype, fp8, device) -> DispatchOut:
-    pdt = torch.uint8 if fp8 else x_dtype
+def alloc_dispatch(T, H, K, E, packed_rows, x_dtype, fp8, device, fp4=False) -> DispatchOut:
+    """Output buffers of a dispatch; fp4 rows hold two e2m1 codes per byte."""
+    q = fp8 or fp4
+    pdt = torch.uint8 if q else x_dtype
     return DispatchOut(
-        packed=torch.empty((packed_rows, H), dtype=pdt, device=device),
-        scales=torch.empty((packed_rows, H // 128), dtype=torch.float32, device=device) if fp8 else None,
+        packed=torch.empty((packed_rows, H // 2 if fp4 else H), dtype=pdt, device=device),
+        scales=torch.empty((packed_rows, H // 128), dtype=torch.float32, device=device) if q else None,
         packed_cnt=torch.empty(E, dtype=torch.int32, device=device),
         packed_off=torch.empty(E + 1, dtype=torch.int32, device=device),
         packed_src=torch.empty(packed_rows, dtype=torch.int32, device=device),
@@ -164,17 +167,18 @@ def alloc_dispatch(T, H, K, E, packed_rows, x_dtype, fp8, device) -> DispatchOut
 
 def dispatch(x: torch.Tensor, idx: torch.Tensor, E: int, cap: int = 0,
              packed_rows: Optional[int] = None, fp8: bool = False,
-             out: Optional[DispatchOut] = None, ws=None) -> DispatchOut:
+             out: Optional[DispatchOut] = None, ws=None, fp4: bool = False) -> DispatchOut:
     """Count, scan, slot and scatter x [T,H] (bf16 or f32) into per-expert rows.
-    fp8=True packs bf16 to blockwise e4m3 with f32 scales per 128 elements."""
+    fp8=True packs bf16 to blockwise e4m3 with f32 scales per 128 elements;
+    fp4=True to e2m1, two codes per byte, with the same scale blocks."""
     T, H = x.shape
     K = idx.shape[1]
     if packed_rows is None:
         packed_rows = E * cap if cap > 0 else T * K
     dev = x.device
-    o = alloc_dispatch(T, H, K, E, packed_rows, x.dtype, fp8, dev) if out is None else out
+    o = alloc_dispatch(T, H, K, E, packed_rows, x.dtype, fp8, dev, fp4) if out is None else out
     ws = _ws(ws, T, K, E, 0, dev)
-    pdt = MOE_FP8_E4M3 if fp8 else dtype_code(x.dtype)
+    pdt = MOE_FP4_E2M1 if fp4 else (MOE_FP8_E4M3 if fp8 else dtype_code(x.dtype))
     _check(load().moe_dispatch(ptr(x), dtype_code(x.dtype), T, H, ptr(idx), K, E, cap,
                                packed_rows, ptr(o.packed), pdt, ptr(o.scales), ptr(o.packed_cnt),
                                ptr(o.packed_off), ptr(o.packed_src), ptr(o.tok_map), ptr(o.stats),
@@ -204,15 +208,16 @@ def dispatch_prequant(x_q: torch.Tensor, x_scales: torch.Tensor, idx: torch.Tens
 
 def dispatch_replay(x: torch.Tensor, tok_map: torch.Tensor, packed: torch.Tensor,
                     scales: Optional[torch.Tensor] = None,
-                    x_scales: Optional[torch.Tensor] = None) -> torch.Tensor:
+                    x_scales: Optional[torch.Tensor] = None, fp4: bool = False) -> torch.Tensor:
     """Move the rows of x [T,H] into packed along a cached tok_map [T,K] (no
-    routing).  packed uint8 with x bf16 packs to fp8 (scales out); x uint8 with
-    x_scales is pre-quantized input."""
+    routing).  packed uint8 with x bf16 packs to fp8 (fp4=True: e2m1, [rows,H/2])
+    with scales out; x uint8 with x_scales is pre-quantized fp8 input."""
     T, H = x.shape
     K = tok_map.shape[1]
     dev = x.device
     x_dt = MOE_FP8_E4M3 if x.dtype == torch.uint8 else dtype_code(x.dtype)
-    pdt = MOE_FP8_E4M3 if packed.dtype == torch.uint8 else dtype_code(packed.dtype)
+    pdt = MOE_FP4_E2M1 if fp4 else (MOE_FP8_E4M3 if packed.dtype == torch.uint8
+                                     else dtype_code(packed.dtype))
     _check(load().moe_dispatch_replay(ptr(x), x_dt, ptr(x_scales), T, H, ptr(tok_map), K,
                                       packed.shape[0], ptr(packed), pdt, ptr(scales),
                                       _stream(dev)))
@@ -255,6 +260,24 @@ def combine_fp8(q: torch.Tensor, scales: Optional[torch.Tensor], tok_map: torch.
     if want_weights and out_weights is None:
         out_weights = torch.empty(T, dtype=torch.float32, device=dev)
     _check(load().moe_combine_fp8(ptr(q), ptr(scales), y_rows, H, ptr(tok_map), ptr(w), T, K,
+                                  ptr(out), dtype_code(out.dtype), ptr(out_weights), _stream(dev)))
+    return out, out_weights
+
+
+def combine_fp4(q: torch.Tensor, scales: Optional[torch.Tensor], tok_map: torch.Tensor,
+                w: torch.Tensor, out_dtype: torch.dtype = torch.bfloat16,
+                out: Optional[torch.Tensor] = None, out_weights: Optional[torch.Tensor] = None,
+                want_weights: bool = True):
+    """Combine of fp4 expert outputs: q uint8 [rows,H/2] (two e2m1 codes per
+    byte), scales f32 [rows,H/128] or None; out [T,H] = sum_k w * (f32(q) * s)."""
+    y_rows, Hh = q.shape
+    H = 2 * Hh
+    T, K = tok_map.shape
+    dev = q.device
+    out = torch.empty((T, H), dtype=out_dtype, device=dev) if out is None else out
+    if want_weights and out_weights is None:
+        out_weights = torch.empty(T, dtype=torch.float32, device=dev)
+    _check(load().moe_combine_fp4(ptr(q), ptr(scales), y_rows, H, ptr(tok_map), ptr(w), T, K,
                                   ptr(out), dtype_code(out.dtype), ptr(out_weights), _stream(dev)))
     return out, out_weights
 

@@ -44,6 +44,8 @@ size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 int elem_bytes(moe_dtype d) { return d == MOE_F32 ? 4 : (d == MOE_BF16 ? 2 : 1); }
 
+bool quantized(moe_dtype d) { return d == MOE_FP8_E4M3 || d == MOE_FP4_E2M1; }
+
 // Workspace carving.  Sizes depend only on (T, K, E, R).
 struct Carve {
     size_t total = 0;
@@ -267,11 +269,15 @@ int check_payload(const void* x, moe_dtype x_dt, const float* x_scales, int64_t 
                   const float* packed_scales) {
     if (x_dt != MOE_BF16 && x_dt != MOE_F32 && x_dt != MOE_FP8_E4M3)
         return fail(MOE_ERR_INVALID_ARG, "x dtype must be MOE_BF16, MOE_F32 or MOE_FP8_E4M3");
-    const bool fp8_out = packed_dt == MOE_FP8_E4M3;
+    if (packed_dt != MOE_BF16 && packed_dt != MOE_F32 && !quantized(packed_dt))
+        return fail(MOE_ERR_INVALID_ARG, "unknown packed dtype %d", (int)packed_dt);
+    const bool fp8_out = quantized(packed_dt);
     if (packed_dt != x_dt && !fp8_out)
-        return fail(MOE_ERR_INVALID_ARG, "packed dtype must equal x dtype or be MOE_FP8_E4M3");
+        return fail(MOE_ERR_INVALID_ARG, "packed dtype must equal x dtype or be fp8/fp4");
     if (fp8_out && x_dt == MOE_F32)
-        return fail(MOE_ERR_UNSUPPORTED, "fp8 packing is implemented for bf16 input only");
+        return fail(MOE_ERR_UNSUPPORTED, "fp8/fp4 packing is implemented for bf16 input only");
+    if (x_dt == MOE_FP8_E4M3 && packed_dt != MOE_FP8_E4M3)
+        return fail(MOE_ERR_INVALID_ARG, "pre-quantized fp8 input goes to fp8 rows");
     MOE_TRY(check_H(H, fp8_out));
     if (packed_rows < 0 || packed_rows > kMaxRows)
         return fail(MOE_ERR_INVALID_ARG, "packed_rows must be in [0, 2^31-1]");
@@ -301,7 +307,8 @@ moe::ScatterArgs scatter_args(const void* x, moe_dtype x_dt, const float* x_scal
     sa.T = T;
     sa.H = H;
     sa.x_bytes = elem_bytes(x_dt);
-    sa.fp8 = packed_dt == MOE_FP8_E4M3 && x_dt == MOE_BF16;
+    sa.fp8 = quantized(packed_dt) && x_dt == MOE_BF16;
+    sa.fp4 = packed_dt == MOE_FP4_E2M1;
     sa.replay = false;
     sa.packed = packed_x;
     sa.scales = packed_scales;
@@ -442,9 +449,11 @@ MOE_API int moe_combine(const void* y, moe_dtype y_dt, int64_t y_rows, int64_t H
     return ok();
 }
 
-MOE_API int moe_combine_fp8(const uint8_t* q, const float* scales, int64_t y_rows, int64_t H,
-                            const int64_t* tok_map, const float* w, int64_t T, int K, void* out,
-                            moe_dtype out_dt, float* out_weights, void* stream) {
+namespace {
+
+int combine_quant(const uint8_t* q, bool fp4, const float* scales, int64_t y_rows, int64_t H,
+                  const int64_t* tok_map, const float* w, int64_t T, int K, void* out,
+                  moe_dtype out_dt, float* out_weights, void* stream, const char* name) {
     if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T must be >= 0");
     if (K < 1 || K > 16) return fail(MOE_ERR_INVALID_ARG, "K=%d must be in [1,16]", K);
     if (out_dt != MOE_BF16 && out_dt != MOE_F32)
@@ -462,6 +471,7 @@ MOE_API int moe_combine_fp8(const uint8_t* q, const float* scales, int64_t y_row
     moe::CombineArgs a{};
     a.y = q;
     a.y_fp8 = true;
+    a.y_fp4 = fp4;
     a.y_scales = scales;
     a.y_rows = y_rows;
     a.H = H;
@@ -472,8 +482,24 @@ MOE_API int moe_combine_fp8(const uint8_t* q, const float* scales, int64_t y_row
     a.out = out;
     a.out_f32 = out_dt == MOE_F32;
     a.out_weights = out_weights;
-    MOE_HIP(moe::launch_combine(a, (hipStream_t)stream), "moe_combine_fp8");
+    MOE_HIP(moe::launch_combine(a, (hipStream_t)stream), name);
     return ok();
+}
+
+}  // namespace
+
+MOE_API int moe_combine_fp8(const uint8_t* q, const float* scales, int64_t y_rows, int64_t H,
+                            const int64_t* tok_map, const float* w, int64_t T, int K, void* out,
+                            moe_dtype out_dt, float* out_weights, void* stream) {
+    return combine_quant(q, false, scales, y_rows, H, tok_map, w, T, K, out, out_dt, out_weights,
+                         stream, "moe_combine_fp8");
+}
+
+MOE_API int moe_combine_fp4(const uint8_t* q, const float* scales, int64_t y_rows, int64_t H,
+                            const int64_t* tok_map, const float* w, int64_t T, int K, void* out,
+                            moe_dtype out_dt, float* out_weights, void* stream) {
+    return combine_quant(q, true, scales, y_rows, H, tok_map, w, T, K, out, out_dt, out_weights,
+                         stream, "moe_combine_fp4");
 }
 
 MOE_API int moe_dedup_dispatch(const void* x, moe_dtype x_dt, int64_t T, int64_t H,

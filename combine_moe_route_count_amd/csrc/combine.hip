@@ -172,9 +172,10 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(CombineArgs a, in
 // the direct cast), then acc = acc + w_k * v for k ascending.  A lane-unit is
 // 16 elements: one 16-byte load of codes per row (the same bytes in flight as
 // the bf16 form's 8 elements) plus the row's scale, dequantized two codes per
-// v_cvt_pk_f32_fp8 inside the reduce.
+// v_cvt_pk_f32_fp8 inside the reduce.  FP4: e2m1 codes, two per byte, an
+// 8-byte load per row, eight codes per gfx950 scaled conversion (scale 1).
 // ---------------------------------------------------------------------------
-template <bool OF32, int KMAX>
+template <bool OF32, int KMAX, bool FP4>
 __device__ __forceinline__ void combine_fp8_item(const CombineArgs& a, int64_t t, int c, int C) {
     const int64_t H = a.H;
     const int units = (int)(H / 16);
@@ -187,11 +188,13 @@ __device__ __forceinline__ void combine_fp8_item(const CombineArgs& a, int64_t t
     if ((int)threadIdx.x < C && u < units) {
         const uint8_t* q = (const uint8_t*)a.y;
         u32x4 code[KMAX];
+        u32x2 code4[KMAX];
         float scl[KMAX];
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) {
             if (rows[k] < 0) continue;
-            code[k] = ld16_stream(q + (int64_t)rows[k] * H + (int64_t)u * 16);
+            if (FP4) code4[k] = ld8_stream(q + (int64_t)rows[k] * (H / 2) + (int64_t)u * 8);
+            else code[k] = ld16_stream(q + (int64_t)rows[k] * H + (int64_t)u * 16);
             scl[k] = a.y_scales ? a.y_scales[(int64_t)rows[k] * nblk + u / (kFp8Block / 16)] : 1.0f;
         }
         float acc[16];
@@ -200,17 +203,28 @@ __device__ __forceinline__ void combine_fp8_item(const CombineArgs& a, int64_t t
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) {
             if (rows[k] < 0) continue;
+            float v[16];
+            if (FP4) {
+                float h0[8], h1[8];
+                unpack_e2m1x8(code4[k][0], h0);
+                unpack_e2m1x8(code4[k][1], h1);
 #pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                float v[4];
-                unpack_e4m3x2<false>(code[k][d], v[0], v[1]);
-                unpack_e4m3x2<true>(code[k][d], v[2], v[3]);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float dq = v[j] * scl[k];
-                    const float p = w[k] * dq;
-                    acc[4 * d + j] = acc[4 * d + j] + p;
+                for (int j = 0; j < 8; ++j) {
+                    v[j] = h0[j];
+                    v[8 + j] = h1[j];
                 }
+            } else {
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    unpack_e4m3x2<false>(code[k][d], v[4 * d], v[4 * d + 1]);
+                    unpack_e4m3x2<true>(code[k][d], v[4 * d + 2], v[4 * d + 3]);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const float dq = v[j] * scl[k];
+                const float p = w[k] * dq;
+                acc[j] = acc[j] + p;
             }
         }
         float lo[8], hi[8];
@@ -231,12 +245,12 @@ __device__ __forceinline__ void combine_fp8_item(const CombineArgs& a, int64_t t
     }
 }
 
-template <bool OF32, int KMAX>
+template <bool OF32, int KMAX, bool FP4>
 __global__ __launch_bounds__(kCombThreads) void combine_fp8_kernel(CombineArgs a, int C, int nch) {
     const int64_t items = a.T * nch;
     for (int64_t wi = blockIdx.x; wi < items; wi += gridDim.x) {
         const int64_t t = wi / nch;
-        combine_fp8_item<OF32, KMAX>(a, t, (int)(wi - t * nch), C);
+        combine_fp8_item<OF32, KMAX, FP4>(a, t, (int)(wi - t * nch), C);
     }
 }
 
@@ -414,19 +428,19 @@ void by_k(const CombineArgs& a, hipStream_t s) {
 #undef MOE_K_CASE
 }
 
-template <bool OF32, int KMAX>
+template <bool OF32, int KMAX, bool FP4>
 void fp8_go(const CombineArgs& a, hipStream_t s) {
     const Chunking ch = chunking(a.H, 16);
-    combine_fp8_kernel<OF32, KMAX>
+    combine_fp8_kernel<OF32, KMAX, FP4>
         <<<item_grid(a.T * ch.nch), dim3(threads_for(ch.C)), 0, s>>>(a, ch.C, ch.nch);
 }
 
-template <bool OF32>
+template <bool OF32, bool FP4>
 void fp8_by_k(const CombineArgs& a, hipStream_t s) {
-    if (a.K <= 2) fp8_go<OF32, 2>(a, s);
-    else if (a.K <= 4) fp8_go<OF32, 4>(a, s);
-    else if (a.K <= 8) fp8_go<OF32, 8>(a, s);
-    else fp8_go<OF32, 16>(a, s);
+    if (a.K <= 2) fp8_go<OF32, 2, FP4>(a, s);
+    else if (a.K <= 4) fp8_go<OF32, 4, FP4>(a, s);
+    else if (a.K <= 8) fp8_go<OF32, 8, FP4>(a, s);
+    else fp8_go<OF32, 16, FP4>(a, s);
 }
 
 }  // namespace
@@ -434,8 +448,13 @@ void fp8_by_k(const CombineArgs& a, hipStream_t s) {
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
     if (a.T == 0) return hipSuccess;
     if (a.y_fp8) {
-        if (a.out_f32) fp8_by_k<true>(a, s);
-        else fp8_by_k<false>(a, s);
+        if (a.y_fp4) {
+            if (a.out_f32) fp8_by_k<true, true>(a, s);
+            else fp8_by_k<false, true>(a, s);
+        } else {
+            if (a.out_f32) fp8_by_k<true, false>(a, s);
+            else fp8_by_k<false, false>(a, s);
+        }
     } else if (a.y_f32) {
         if (a.out_f32) by_k<true, true>(a, s);
         else by_k<true, false>(a, s);

@@ -22,6 +22,7 @@ constexpr int64_t kMaxGrid = (int64_t)1 << 22;
 
 constexpr int kFp8Block = 128;
 constexpr float kE4m3Max = 448.0f;
+constexpr float kE2m1Max = 6.0f;
 
 // Key codes produced by the routing key functions.
 constexpr int kKeySkip = -1;     // "no expert": skipped, not counted
@@ -29,6 +30,7 @@ constexpr int kKeyInvalid = -2;  // id outside [0, E) other than -1: counted inv
 constexpr int kKeyDropped = -3;  // valid entry dropped before slotting: counted dropped
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------------------
 // wave64 primitives
@@ -108,6 +110,30 @@ __device__ __forceinline__ void unpack_e4m3x2(uint32_t d, float& a, float& b) {
     b = v.y;
 }
 
+// Eight e2m1 (fp4) codes of d -> f32, exact; element 2i is the low nibble of
+// byte i.  The gfx950 scaled converters apply only the exponent of their scale
+// operand, so they are given 1.0 and any block scale is applied in f32 apart.
+__device__ __forceinline__ void unpack_e2m1x8(uint32_t d, float (&v)[8]) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    const f2 a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 0);
+    const f2 b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 1);
+    const f2 c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 2);
+    const f2 e = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 3);
+    v[0] = a.x; v[1] = a.y; v[2] = b.x; v[3] = b.y;
+    v[4] = c.x; v[5] = c.y; v[6] = e.x; v[7] = e.y;
+}
+
+// Eight f32 (|v| <= 6 after the caller's clamp) -> e2m1 codes, round to nearest
+// even, sign kept for zero results; byte i holds elements 2i (low) and 2i+1.
+__device__ __forceinline__ uint32_t pack_e2m1x8(const float (&v)[8]) {
+    uint32_t d = 0;
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, v[0], v[1], 1.0f, 0);
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, v[2], v[3], 1.0f, 1);
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, v[4], v[5], 1.0f, 2);
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, v[6], v[7], 1.0f, 3);
+    return d;
+}
+
 // ---------------------------------------------------------------------------
 // 16-byte memory access
 // ---------------------------------------------------------------------------
@@ -119,6 +145,12 @@ __device__ __forceinline__ u32x4 ld16_stream(const void* p) {
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *(u32x4*)p = v; }
 __device__ __forceinline__ void st16_stream(void* p, u32x4 v) {
     __builtin_nontemporal_store(v, (u32x4*)p);
+}
+__device__ __forceinline__ u32x2 ld8_stream(const void* p) {
+    return __builtin_nontemporal_load((const u32x2*)p);
+}
+__device__ __forceinline__ void st8_stream(void* p, u32x2 v) {
+    __builtin_nontemporal_store(v, (u32x2*)p);
 }
 
 }  // namespace moe

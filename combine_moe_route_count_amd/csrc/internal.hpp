@@ -68,7 +68,8 @@ struct ScatterArgs {
     const float* x_scales;     // pre-quantized input: [T,H/128] forwarded to scales; else null
     int64_t T, H;
     int x_bytes;               // 2 (bf16), 4 (f32) or 1 (pre-quantized e4m3)
-    bool fp8;                  // pack bf16 -> e4m3 + scales
+    bool fp8;                  // pack bf16 -> e4m3 (or, with fp4, e2m1) + scales
+    bool fp4;                  // with fp8: e2m1 codes, two per byte
     bool replay;               // rows from the cached tok_map; tok_map and packed_src not written
     void* packed;
     float* scales;
@@ -139,6 +140,7 @@ struct CombineArgs {
     const void* y;
     bool y_f32;
     bool y_fp8;              // e4m3 codes, dequantized with y_scales (NULL: scale 1)
+    bool y_fp4;              // with y_fp8: e2m1 codes, two per byte
     const float* y_scales;   // [y_rows, H/128]
     int64_t y_rows, H;
     const int64_t* tok_map;

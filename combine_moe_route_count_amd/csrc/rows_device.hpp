@@ -115,4 +115,41 @@ __device__ __forceinline__ void fp8_pack16(const u32x4& lo, const u32x4& hi, u32
         q[j] = pack_e4m3x4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]);
 }
 
+// The same 16 bf16 values packed to e2m1 (fp4): the fp8 block rule with the
+// e2m1 maximum 6 in place of 448; two words of eight codes.
+__device__ __forceinline__ void fp4_pack16(const u32x4& lo, const u32x4& hi, u32x2& q,
+                                           float& scale) {
+    float v[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        v[2 * j] = bf16lo(lo[j]);
+        v[2 * j + 1] = bf16hi(lo[j]);
+        v[8 + 2 * j] = bf16lo(hi[j]);
+        v[8 + 2 * j + 1] = bf16hi(hi[j]);
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(v[j]));
+    amax = group8_max(amax);
+    scale = 1.0f;
+    if (amax > kE2m1Max) {
+        // q = e2m1(clamp((x * 6) / amax)); x * 6 is exact for bf16 x
+        scale = amax / kE2m1Max;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const float n = v[j] * kE2m1Max;
+            const float qv = n / amax;
+            v[j] = fminf(fmaxf(qv, -kE2m1Max), kE2m1Max);
+        }
+    }
+    float a[8], b[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        a[j] = v[j];
+        b[j] = v[8 + j];
+    }
+    q[0] = pack_e2m1x8(a);
+    q[1] = pack_e2m1x8(b);
+}
+
 }  // namespace moe

@@ -90,7 +90,7 @@ __device__ __forceinline__ void scatter_copy_kernel_item(const ScatterArgs& a, i
 // plain dispatch, fused blockwise fp8 pack (bf16 in)
 // ---------------------------------------------------------------------------
 
-template <int DMAX, int UPT, bool REPLAY>
+template <int DMAX, int UPT, bool REPLAY, bool FP4>
 __device__ __forceinline__ void scatter_fp8_kernel_item(const ScatterArgs& a, int64_t t, int nth) {
     const int tid = threadIdx.x;
     const int K = a.slot.K;
@@ -115,22 +115,28 @@ __device__ __forceinline__ void scatter_fp8_kernel_item(const ScatterArgs& a, in
 
     int rows[DMAX];
     token_rows<DMAX, REPLAY>(a, t, rows);
+    const int64_t prow = FP4 ? H / 2 : H;      // bytes per packed row
     for (int base = 0;;) {
         u32x4 q[UPT];
+        u32x2 q4[UPT];
         float s[UPT];
 #pragma unroll
-        for (int i = 0; i < UPT; ++i) fp8_pack16(lo[i], hi[i], q[i], s[i]);
+        for (int i = 0; i < UPT; ++i) {
+            if (FP4) fp4_pack16(lo[i], hi[i], q4[i], s[i]);
+            else fp8_pack16(lo[i], hi[i], q[i], s[i]);
+        }
 #pragma unroll
         for (int d = 0; d < DMAX; ++d) {
             if (d >= K) break;
             if (rows[d] < 0) continue;
-            char* out = (char*)a.packed + (int64_t)rows[d] * H;
+            char* out = (char*)a.packed + (int64_t)rows[d] * prow;
             float* sc = a.scales + (int64_t)rows[d] * nblk;
 #pragma unroll
             for (int i = 0; i < UPT; ++i) {
                 const int u = base + tid + i * nth;
                 if (u < nunits) {
-                    st16_stream(out + (int64_t)u * 16, q[i]);
+                    if (FP4) st8_stream(out + (int64_t)u * 8, q4[i]);
+                    else st16_stream(out + (int64_t)u * 16, q[i]);
                     if ((u & 7) == 0) sc[u >> 3] = s[i];  // cached: L2 merges the 32-byte pieces of a scale row
                 }
             }
@@ -254,10 +260,10 @@ __global__ __launch_bounds__(kCopyThreads) void scatter_copy_kernel(ScatterArgs 
     for (int64_t t = blockIdx.x; t < a.T; t += gridDim.x)
         scatter_copy_kernel_item<DMAX, VPT, REPLAY, SC>(a, t, nth);
 }
-template <int DMAX, int UPT, bool REPLAY>
+template <int DMAX, int UPT, bool REPLAY, bool FP4>
 __global__ __launch_bounds__(kCopyThreads) void scatter_fp8_kernel(ScatterArgs a, int nth) {
     for (int64_t t = blockIdx.x; t < a.T; t += gridDim.x)
-        scatter_fp8_kernel_item<DMAX, UPT, REPLAY>(a, t, nth);
+        scatter_fp8_kernel_item<DMAX, UPT, REPLAY, FP4>(a, t, nth);
 }
 template <int DMAX, int VPT>
 __global__ __launch_bounds__(kCopyThreads) void recv_copy_kernel(RecvArgs a, int nth) {
@@ -360,12 +366,12 @@ struct CopyMode {
         }
     };
 };
-template <bool REPLAY>
+template <bool REPLAY, bool FP4>
 struct Fp8Mode {
     template <int D, int V>
     struct Launch {
         static void go(dim3 g, int th, const ScatterArgs& a, hipStream_t s) {
-            scatter_fp8_kernel<D, V, REPLAY><<<g, dim3(th), 0, s>>>(a, th);
+            scatter_fp8_kernel<D, V, REPLAY, FP4><<<g, dim3(th), 0, s>>>(a, th);
         }
     };
 };
@@ -390,8 +396,11 @@ hipError_t launch_scatter(const ScatterArgs& a, hipStream_t s) {
     if (a.fp8) {
         const int nunits = (int)(a.H / 16);
         const int th = copy_threads<2>(nunits);
-        return a.replay ? by_dmax<Fp8Mode<true>::Launch, 2>(a.slot.K, grid, th, a, s)
-                        : by_dmax<Fp8Mode<false>::Launch, 2>(a.slot.K, grid, th, a, s);
+        if (a.fp4)
+            return a.replay ? by_dmax<Fp8Mode<true, true>::Launch, 2>(a.slot.K, grid, th, a, s)
+                            : by_dmax<Fp8Mode<false, true>::Launch, 2>(a.slot.K, grid, th, a, s);
+        return a.replay ? by_dmax<Fp8Mode<true, false>::Launch, 2>(a.slot.K, grid, th, a, s)
+                        : by_dmax<Fp8Mode<false, false>::Launch, 2>(a.slot.K, grid, th, a, s);
     }
     const int nvec = (int)(a.H * a.x_bytes / 16);
     const int th = copy_threads<4>(nvec);

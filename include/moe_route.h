@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-typedef enum { MOE_BF16 = 0, MOE_F32 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
+typedef enum { MOE_BF16 = 0, MOE_F32 = 1, MOE_FP8_E4M3 = 2, MOE_FP4_E2M1 = 3 } moe_dtype;
 
 typedef enum {
     MOE_OK = 0,
@@ -105,11 +105,14 @@ int moe_route_count(const int32_t* idx, int64_t T, int K, int E, int32_t* cnt, i
  *   x            [T,H] x_dt (MOE_BF16 or MOE_F32)
  *   cap          > 0: padded layout, rows [e*cap, e*cap+cap); 0: compact layout
  *   packed_rows  rows of packed_x (and packed_src, packed_scales)
- *   packed_x     out [packed_rows,H] packed_dt: x_dt, or MOE_FP8_E4M3 from MOE_BF16
- *   packed_scales out f32 [packed_rows,H/128] iff packed_dt == MOE_FP8_E4M3, else NULL.
- *                Per block: amax = max|x|; amax > 448 gives s = amax/448 and
- *                q = e4m3((x*448)/amax); otherwise s = 1 and q = e4m3(x);
- *                e4m3 rounds to nearest even.
+ *   packed_x     out [packed_rows,H] packed_dt: x_dt, or MOE_FP8_E4M3 / MOE_FP4_E2M1
+ *                from MOE_BF16 (fp4: [packed_rows,H/2] bytes, two codes per byte,
+ *                element 2i in the low nibble)
+ *   packed_scales out f32 [packed_rows,H/128] iff packed_dt is fp8 or fp4, else NULL.
+ *                Per block, with M = 448 (e4m3) or 6 (e2m1): amax = max|x|;
+ *                amax > M gives s = amax/M and q = enc((x*M)/amax); otherwise
+ *                s = 1 and q = enc(x); enc rounds to nearest even (the fp4 rule
+ *                is the fp8 rule of the pages carried to the e2m1 maximum).
  *   packed_cnt   out int32 [E]   rows written per expert
  *   packed_off   out int32 [E+1] first row of each expert's segment,
  *                min(e*cap or off[e], packed_rows); may be NULL
@@ -229,6 +232,15 @@ int moe_dedup_dispatch(const void* x, moe_dtype x_dt, int64_t T, int64_t H, cons
  * decoding of q.  Errors: MOE_ERR_INVALID_ARG for the checks of moe_combine
  * and H % 128 != 0; enqueues nothing on error.  The dedup plan is not taken. */
 int moe_combine_fp8(const uint8_t* q, const float* scales, int64_t y_rows, int64_t H,
+                    const int64_t* tok_map, const float* w, int64_t T, int K, void* out,
+                    moe_dtype out_dt, float* out_weights, void* stream);
+
+/* Combine of fp4 expert outputs ("Draft: cco + flydsl dispatch/combine",
+ * commit adding the fp4 e2m1 accum path: 8 packed codes per i32, expanded to
+ * f32 with the gfx950 scaled conversions): as moe_combine_fp8 with q holding
+ * e2m1 codes, [y_rows,H/2] bytes, element 2i in the low nibble of byte i;
+ * v = f32(e2m1(q)) * scales[row][h/128] (1 if scales NULL). */
+int moe_combine_fp4(const uint8_t* q, const float* scales, int64_t y_rows, int64_t H,
                     const int64_t* tok_map, const float* w, int64_t T, int K, void* out,
                     moe_dtype out_dt, float* out_weights, void* stream);
 

@@ -46,16 +46,16 @@ def poison_(t) -> None:
         t.view(torch.uint8).fill_(oracle.POISON_BYTE)
 
 
-def gpu_dispatch(x_dev, idx_np, E, cap=0, packed_rows=None, fp8=False):
+def gpu_dispatch(x_dev, idx_np, E, cap=0, packed_rows=None, fp8=False, fp4=False):
     T, H = x_dev.shape
     K = idx_np.shape[1]
     if packed_rows is None:
         packed_rows = E * cap if cap > 0 else T * K
-    o = moe._lib.alloc_dispatch(T, H, K, E, packed_rows, x_dev.dtype, fp8, DEV)
+    o = moe._lib.alloc_dispatch(T, H, K, E, packed_rows, x_dev.dtype, fp8, DEV, fp4=fp4)
     for t in (o.packed, o.scales, o.packed_src, o.tok_map, o.packed_cnt, o.packed_off, o.stats):
         poison_(t)
     moe.dispatch(x_dev, dev(idx_np.astype(np.int32)), E, cap=cap, packed_rows=packed_rows,
-                 fp8=fp8, out=o)
+                 fp8=fp8, out=o, fp4=fp4)
     torch.cuda.synchronize()
     return o
 

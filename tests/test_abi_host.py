@@ -121,6 +121,18 @@ def c8(**kw):
                              a["out"], a["odt"], a["ow"], None)
     return [st, lib.moe_last_error().decode()]
 
+def c4(**kw):
+    a = dict(q=A, sc=A, yr=10, H=128, tm=A, w=A, T=5, K=2, out=A, odt=0, ow=None)
+    a.update(kw)
+    st = lib.moe_combine_fp4(a["q"], a["sc"], a["yr"], a["H"], a["tm"], a["w"], a["T"], a["K"],
+                             a["out"], a["odt"], a["ow"], None)
+    return [st, lib.moe_last_error().decode()]
+
+res["combine_fp4"] = {"H64": c4(H=64), "K0": c4(K=0), "out_fp4": c4(odt=3), "q_unaligned": c4(q=A8)}
+res["dispatch"]["fp4_from_f32"] = disp(x_dt=1, pdt=3, scales=A, H=128)
+res["dispatch"]["fp4_no_scales"] = disp(pdt=3, H=128)
+res["dispatch"]["fp4_H64"] = disp(pdt=3, scales=A, H=64)
+res["dispatch"]["bad_packed_dtype"] = disp(pdt=9)
 res["combine_fp8"] = {
     "H64": c8(H=64), "K0": c8(K=0), "K17": c8(K=17), "out_fp8": c8(odt=2), "q_null": c8(q=None),
     "q_unaligned": c8(q=A8), "scales_unaligned": c8(sc=P(0x100002)), "tm_null": c8(tm=None),
@@ -206,7 +218,7 @@ def test_dispatch_argument_errors():
     for case, (st, msg) in d.items():
         if case in expect_ws:
             assert st == WORKSPACE, (case, st, msg)
-        elif case == "fp8_from_f32":
+        elif case in ("fp8_from_f32", "fp4_from_f32"):
             assert st == UNSUPPORTED, (case, st, msg)
         else:
             assert st == INVALID, (case, st, msg)
@@ -228,6 +240,8 @@ def test_dedup_and_helpers_argument_errors():
         assert st == (UNSUPPORTED if case == "f32_to_fp8" else INVALID) and msg, (case, st, msg)
     for case, (st, msg) in _res()["prequant"].items():
         assert st == (WORKSPACE if case == "ws_small" else INVALID) and msg, (case, st, msg)
+    for case, (st, msg) in _res()["combine_fp4"].items():
+        assert st == INVALID and msg, (case, st, msg)
     for case, (st, msg) in _res()["combine_fp8"].items():
         assert st == INVALID and msg, (case, st, msg)
     for case, (st, msg) in _res()["copy16"].items():

@@ -634,3 +634,93 @@ def test_dispatch_replay_equals_routed_dispatch():
     assert torch.equal(packed, o2.packed)
     assert torch.equal(scales.view(torch.int32), o2.scales.view(torch.int32))
 
+
+# ---------------------------------------------------------------------------
+# fp4 (e2m1) payload
+# ---------------------------------------------------------------------------
+
+def test_fp4_encoder_exhaustive_via_dispatch():
+    """Every bf16 value with |v| <= 6 goes through the unscaled branch once; the
+    finite values up to 448 fill scaled rows (arbitrary f32 quotients)."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    v = W.f32_from_bf16_bits(bits)
+    small = bits[np.isfinite(v) & (np.abs(v) <= 6)]
+    big = bits[np.isfinite(v) & (np.abs(v) <= 448)]
+    H = 1024
+    n = (len(small) + H - 1) // H * H
+    xs = np.resize(small, n).reshape(-1, H)
+    rng = np.random.default_rng(4)
+    nb = (len(big) + H - 1) // H * H
+    sc = rng.permutation(np.resize(big, nb)).reshape(-1, H)
+    scf = W.f32_from_bf16_bits(sc)
+    scf[:, ::131] = np.float32(3000.0)
+    x = np.concatenate([xs, W.bf16_bits_from_f32(scf)])
+    T = x.shape[0]
+    idx = np.zeros((T, 1), np.int32)
+    note(f"fp4 exhaustive T={T} H={H}")
+    o = gpu_dispatch(dev_bf16(x), idx, 1, fp4=True)
+    ref = oracle.dispatch(x, "bf16", idx, 1, packed_dt="fp4")
+    assert_dispatch_equal(o, ref, fp8=True)
+
+
+@pytest.mark.parametrize("layout", ["compact", "padded_tight", "compact_short"])
+@pytest.mark.parametrize("T,K,E,H", [(300, 4, 13, 128), (2100, 8, 256, 384)])
+def test_dispatch_fp4_small(layout, T, K, E, H):
+    rng = np.random.default_rng(T + K * 3 + H)
+    idx = _mixed_idx(rng, T, K, E)
+    x = W.inject_outliers(W.normal_x(rng, T, H, "bf16"), np.arange(0, T, 17), 100.0)
+    flat = idx.ravel()
+    cnt = np.bincount(flat[(flat >= 0) & (flat < E)], minlength=E)
+    cap = {"compact": 0, "padded_tight": max(1, int(cnt.max()) // 2), "compact_short": 0}[layout]
+    rows = {"compact": T * K, "padded_tight": E * cap - 3,
+            "compact_short": max(0, int(cnt.sum()) - 37)}[layout]
+    note(f"dispatch fp4 {layout} T={T} K={K} E={E} H={H}")
+    o = gpu_dispatch(dev_bf16(x), idx, E, cap=cap, packed_rows=rows, fp4=True)
+    ref = oracle.dispatch(x, "bf16", idx, E, cap=cap, packed_rows=rows, packed_dt="fp4")
+    assert_dispatch_equal(o, ref, fp8=True)
+
+
+@pytest.mark.parametrize("out_dt", ["bf16", "f32"])
+@pytest.mark.parametrize("K,H,T,scaled", [(1, 128, 37, True), (3, 384, 300, False), (8, 7168, 129, True),
+                                          (16, 256, 513, True)])
+def test_combine_fp4_random(out_dt, K, H, T, scaled):
+    rng = np.random.default_rng(K * 100 + H + T + 1)
+    rows = max(T * K // 2, K)
+    q = rng.integers(0, 256, size=(rows, H // 2), dtype=np.uint8)
+    sc = (rng.random((rows, H // 128)) * 8 + 2.0 ** -6).astype(np.float32) if scaled else None
+    tm = rng.integers(-1, rows, size=(T, K)).astype(np.int64)
+    tm[rng.random((T, K)) < 0.02] = rows + 3
+    w = rng.standard_normal((T, K)).astype(np.float32)
+    note(f"combine_fp4 K={K} H={H} T={T} scaled={scaled} out={out_dt}")
+    odt = torch.float32 if out_dt == "f32" else torch.bfloat16
+    out = torch.empty((T, H), dtype=odt, device=DEV)
+    ow = torch.empty(T, dtype=torch.float32, device=DEV)
+    poison_(out)
+    poison_(ow)
+    moe.combine_fp4(dev(q), dev(sc) if scaled else None, dev(tm), dev(w), out=out, out_weights=ow)
+    torch.cuda.synchronize()
+    exp, ew = oracle.combine_fp4(q, sc, tm, w, out_dt)
+    _check_combine(host(out), exp, out_dt)
+    np.testing.assert_array_equal(host(ow), ew)
+
+
+def test_fp4_end_to_end_skewed_full():
+    """The metric shape with an fp4 payload: dispatch packs, the packed rows are
+    the expert outputs (identity expert), combine_fp4 reduces; and a replay of
+    the same map reproduces the packed rows."""
+    d = W.make_inputs("skewed_fp8")
+    x = W.inject_outliers(d["x"], np.arange(0, d["T"], 97), 1000.0)
+    note("fp4 end to end skewed T=8192")
+    o = gpu_dispatch(dev_bf16(x), d["idx"], d["E"], fp4=True)
+    out, ow = moe.combine_fp4(o.packed, o.scales, o.tok_map, dev(d["w"]))
+    packed = torch.empty_like(o.packed)
+    scales = torch.empty_like(o.scales)
+    moe.dispatch_replay(dev_bf16(x), o.tok_map, packed, scales=scales, fp4=True)
+    torch.cuda.synchronize()
+    ref = oracle.dispatch(x, "bf16", d["idx"], d["E"], packed_dt="fp4")
+    assert_dispatch_equal(o, ref, fp8=True)
+    exp, ew = oracle.combine_fp4(ref["packed"], ref["scales"], ref["tok_map"], d["w"], "bf16")
+    assert _check_combine(host(out), exp, "bf16")
+    np.testing.assert_array_equal(host(ow), ew)
+    assert torch.equal(packed, o.packed) and torch.equal(scales.view(torch.int32), o.scales.view(torch.int32))
+
