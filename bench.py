@@ -131,32 +131,56 @@ def pmc_summary(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, out_json):
     print(json.dumps(d, indent=1))
 
 
-def cpu_baseline(name, T_full, sample_T):
-    """The oracle, as it stands, on a bounded sample of the same workload."""
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(name, T_full, sample_T, bytes_full):
+    """The oracle, as it stands, on a bounded sample of the same workload: all
+    threads OpenMP gives it on T=sample_T, and one thread on a quarter of that."""
     import numpy as np
     import oracle
     import workloads as W
-    d = W.make_inputs(name, T=sample_T)
-    E = d["E"]
-    fp8 = d["packed_dtype"] == "fp8"
-    times = []
-    for rep in range(3):
-        t0 = time.perf_counter()
-        ref = oracle.dispatch(d["x"], "bf16", d["idx"], E, packed_dt="fp8" if fp8 else None)
-        t1 = time.perf_counter()
-        y = oracle.fp8_dequant(ref["packed"], ref["scales"]) if fp8 else ref["packed"]
-        t2 = time.perf_counter()
-        oracle.combine(y, "bf16", ref["tok_map"], d["w"], "bf16")
-        t3 = time.perf_counter()
-        if rep > 0:                      # first run warms the page cache and allocator
-            times.append((t1 - t0) + (t3 - t2))
-    med = statistics.median(times)
-    us_full = med * 1e6 * (T_full / sample_T)
-    return {"value": round(us_full, 1), "unit": "us/call", "cores": oracle.get_threads(),
-            "kind": "oracle",
-            "sample": f"{name} workload with T={sample_T} tokens (H={d['H']}, E={E}, K={d['K']}), "
-                      f"dispatch+combine timed (median of 2 after 1 warmup), scaled by "
-                      f"{T_full}/{sample_T} to one full call; expert step excluded"}
+
+    def run(T, reps):
+        d = W.make_inputs(name, T=T)
+        E = d["E"]
+        fp8 = d["packed_dtype"] == "fp8"
+        times = []
+        for rep in range(reps):
+            t0 = time.perf_counter()
+            ref = oracle.dispatch(d["x"], "bf16", d["idx"], E, packed_dt="fp8" if fp8 else None)
+            t1 = time.perf_counter()
+            y = oracle.fp8_dequant(ref["packed"], ref["scales"]) if fp8 else ref["packed"]
+            t2 = time.perf_counter()
+            oracle.combine(y, "bf16", ref["tok_map"], d["w"], "bf16")
+            t3 = time.perf_counter()
+            if rep > 0:                  # first run warms the page cache and allocator
+                times.append((t1 - t0) + (t3 - t2))
+        return statistics.median(times) * 1e6 * (T_full / T)
+
+    threads = oracle.get_threads()
+    us_all = run(sample_T, 3)
+    t1_sample = max(sample_T // 4, 1)
+    oracle.set_threads(1)
+    try:
+        us_one = run(t1_sample, 2)
+    finally:
+        oracle.set_threads(threads)
+    return {"value": round(us_all, 1), "unit": "us/call", "cores": threads, "kind": "oracle",
+            "sample": f"{name} workload with T={sample_T} tokens, dispatch+combine timed (median "
+                      f"of 2 after 1 warmup), scaled by {T_full}/{sample_T} to one full call; "
+                      f"expert step excluded",
+            "gbps": round(bytes_full / (us_all * 1e-6) / 1e9, 2),
+            "single_thread_value": round(us_one, 1),
+            "single_thread_sample": f"T={t1_sample}, 1 warmup + 1 timed, scaled by {T_full}/{t1_sample}",
+            "cpu_model": _cpu_model()}
 
 
 def measure(moe, W, name, args, dev, graphs=True, y_fp8=False, fp4=False):
@@ -481,7 +505,7 @@ def main():
     cpu = None
     if not args.no_cpu:
         log(f"[bench] cpu oracle baseline on T={args.cpu_sample} sample ...")
-        cpu = cpu_baseline(name, r["T"], args.cpu_sample)
+        cpu = cpu_baseline(name, r["T"], args.cpu_sample, r["disp_b"] + r["comb_b"])
         log(f"[bench] cpu oracle: {cpu['value']} us/call on {cpu['cores']} threads")
 
     line = {
