@@ -372,6 +372,90 @@ def dispatch_variants(moe, W, name, args, dev):
     return res
 
 
+def dedup_line(moe, W, args, dev, name="dedup"):
+    """The virtual-rank dedup path on its workload (T=16384 H=4096 E=64 K=6 R=8,
+    f32): moe_dedup_dispatch (one recv row per unique (token, rank), then the
+    local expansion) and the dedup combine, fused (per-rank partials kept in
+    registers) and two-stage (partials written to and read back from HBM, the
+    form whose partial rows would cross the links when sharded).  The packed
+    rows serve as the expert outputs (identity expert, copied once per set)."""
+    import numpy as np
+    import torch
+    d = W.make_inputs(name)
+    T, H, E, K, R = d["T"], d["H"], d["E"], d["K"], d["R"]
+    stream = torch.cuda.current_stream(dev)
+    idx = torch.from_numpy(d["idx"]).to(dev)
+    w = torch.from_numpy(d["w"]).to(dev)
+    x0 = torch.from_numpy(d["x"]).to(dev)
+    rr = T * min(K, R)
+    ws = moe.workspace(T, K, E, R, dev)
+    sets = []
+    for _ in range(args.sets):
+        x = x0.clone()
+        o = moe.dedup_dispatch(x, idx, E, R, ws=ws)
+        y = o.packed.clone()
+        sets.append(dict(x=x, o=o, y=y, out=torch.empty((T, H), dtype=torch.float32, device=dev),
+                         ow=torch.empty(T, dtype=torch.float32, device=dev)))
+    partial = torch.empty((rr, H), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    n_recv = int(sets[0]["o"].recv_cnt.sum().item())
+    n_rows = int(sets[0]["o"].packed_cnt.sum().item())
+    assert int(sets[0]["o"].stats[2].item()) == 0, "recv rows dropped"
+
+    def plan(st, two_stage):
+        return dict(R=R, idx=idx, rank_slot=st["o"].rank_slot, recv_rows=rr,
+                    partial=partial if two_stage else None)
+
+    def step(st, ev=None, two_stage=False):
+        if ev: ev[0].record(stream)
+        moe.dedup_dispatch(st["x"], idx, E, R, out=st["o"], ws=ws)
+        if ev: ev[1].record(stream)
+        moe.combine(st["y"], st["o"].tok_map, w, E=E, out_dtype=torch.float32,
+                    dedup=plan(st, two_stage), out=st["out"], out_weights=st["ow"])
+        if ev: ev[2].record(stream)
+
+    res = {}
+    for two_stage in (False, True):
+        for i in range(args.warmup):
+            step(sets[i % len(sets)], two_stage=two_stage)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            step(sets[i % len(sets)], ev[i], two_stage)
+        torch.cuda.synchronize()
+        tail = lambda v: v[1:] if len(v) > 2 else v
+        res[two_stage] = (statistics.median(tail([e[0].elapsed_time(e[2]) * 1e3 for e in ev])),
+                          statistics.median(tail([e[0].elapsed_time(e[1]) * 1e3 for e in ev])),
+                          statistics.median(tail([e[1].elapsed_time(e[2]) * 1e3 for e in ev])))
+    st = sets[0]
+    ow_err = float((st["ow"] - 1.0).abs().max().item())
+    assert ow_err < 1e-5, ow_err
+    del sets, partial
+    torch.cuda.empty_cache()
+    eb = 4
+    row = H * eb
+    meta_d = T * K * 4 + T * K * 8 + n_rows * 4 + n_recv * 4 + T * R * 4
+    disp_b = T * row + 2 * n_recv * row + n_rows * row + meta_d
+    comb_fused = n_rows * row + T * row + T * K * 16 + T * R * 4 + T * 4
+    comb_two = comb_fused + 2 * n_recv * row
+    gb = lambda b, us: round(b / (us * 1e-6) / 1e9, 1)
+    pair_f, disp_f, comb_f = res[False]
+    pair_t, disp_t, comb_t = res[True]
+    out = {"workload": name, "T": T, "H": H, "E": E, "K": K, "R": R, "dtype": "f32",
+           "recv_rows": n_recv, "packed_rows": n_rows,
+           "dispatch_us": round(disp_f, 2), "dispatch_gbps": gb(disp_b, disp_f),
+           "combine_fused_us": round(comb_f, 2), "combine_fused_gbps": gb(comb_fused, comb_f),
+           "pair_fused_us": round(pair_f, 2),
+           "pair_fused_pct_hbm_peak": round(100 * (disp_b + comb_fused) / (pair_f * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
+           "combine_two_stage_us": round(comb_t, 2), "combine_two_stage_gbps": gb(comb_two, comb_t),
+           "pair_two_stage_us": round(pair_t, 2),
+           "pair_two_stage_pct_hbm_peak": round(100 * (disp_b + comb_two) / (pair_t * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
+           "algorithmic_bytes": {"dispatch": disp_b, "combine_fused": comb_fused,
+                                 "combine_two_stage": comb_two}}
+    log(f"[bench] dedup: dispatch {disp_f:.1f} us ({out['dispatch_gbps']} GB/s), combine fused "
+        f"{comb_f:.1f} us, two-stage {comb_t:.1f} us; pair {pair_f:.1f} / {pair_t:.1f} us")
+    return out
+
+
 def copy_ceiling(moe, dev, reps=10):
     """GB/s (bytes read + written) of the library's 16-byte streaming copy of
     1 GiB, on the same stream as the kernels."""
@@ -404,6 +488,7 @@ def main():
     ap.add_argument("--secondary", default="uniform_bf16",
                     help="second workload reported inside the line ('none' to skip)")
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay pass")
+    ap.add_argument("--no-dedup", action="store_true", help="skip the dedup workload line")
     ap.add_argument("--no-fp8-combine", action="store_true",
                     help="skip the line that feeds the fp8 rows straight to moe_combine_fp8")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -499,6 +584,10 @@ def main():
     if r["fp8"] and not args.no_fp8_combine:
         dv = dispatch_variants(moe, W, name, args, dev)
 
+    dd = None
+    if not args.no_dedup:
+        dd = dedup_line(moe, W, args, dev)
+
     copy_gbs = copy_ceiling(moe, dev)
     log(f"[bench] 16-byte streaming copy of 1 GiB: {copy_gbs:.0f} GB/s (read + write)")
 
@@ -546,6 +635,7 @@ def main():
         "fp8_combine": f8,
         "fp4_payload": f4,
         "dispatch_variants": dv,
+        "dedup": dd,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -32,6 +32,8 @@ struct Unit;
 template <>
 struct Unit<false> {  // bf16: one 16-byte load
     u32x4 a;
+    __device__ __forceinline__ void clear() { a = u32x4{0, 0, 0, 0}; }
+    __device__ __forceinline__ void settle() { asm volatile("" : "+v"(a)); }
     __device__ __forceinline__ void load(const void* y, int64_t row, int64_t H, int64_t col) {
         a = ld16_stream((const uint16_t*)y + row * H + col);
     }
@@ -43,6 +45,11 @@ struct Unit<false> {  // bf16: one 16-byte load
 template <>
 struct Unit<true> {  // f32: two 16-byte loads
     u32x4 a, b;
+    __device__ __forceinline__ void clear() {
+        a = u32x4{0, 0, 0, 0};
+        b = u32x4{0, 0, 0, 0};
+    }
+    __device__ __forceinline__ void settle() { asm volatile("" : "+v"(a), "+v"(b)); }
     __device__ __forceinline__ void load(const void* y, int64_t row, int64_t H, int64_t col) {
         const float* p = (const float*)y + row * H + col;
         a = ld16_stream(p);
@@ -259,33 +266,59 @@ __global__ __launch_bounds__(kCombThreads) void combine_fp8_kernel(CombineArgs a
 //   MODE 0: per-rank partials kept in registers, out written (one kernel)
 //   MODE 1: per-rank partials written to `partial` (stage A)
 // ---------------------------------------------------------------------------
+// Routing of token t for the dedup forms, every load in flight together:
+// lanes below K read tok_map, w and idx, lanes below R read rank_slot.  The
+// entries are broadcast to the wave; rank r's recv row stays in lane r and is
+// fetched with recv_row(r), so the per-rank loops do no memory access.
 template <int KMAX>
-__device__ __forceinline__ void entry_ranks(const CombineArgs& a, int64_t t, int (&ranks)[KMAX]) {
+struct DedupToken {
+    int rows[KMAX];
+    float w[KMAX];
+    int ranks[KMAX];
+    int my_rs;    // lane r: recv row of rank r, or -1
+    __device__ __forceinline__ int recv_row(int r) const { return readlane(my_rs, r); }
+};
+
+template <int KMAX>
+__device__ __forceinline__ void dedup_token(const CombineArgs& a, int64_t t, DedupToken<KMAX>& d) {
     const int lane = threadIdx.x % kWave;
     const int er = a.E / a.R;
-    int my_rank = -1;
+    int my_row = -1, my_rank = -1, my_rs = -1;
+    float my_w = 0.0f;
     if (lane < a.K) {
+        const int64_t r = a.tok_map[t * a.K + lane];
+        const float wk = a.w[t * a.K + lane];
         const int32_t e = a.idx[t * a.K + lane];
+        if (r >= 0 && r < a.y_rows) {
+            my_row = (int)r;
+            my_w = wk;
+        }
         if (e >= 0 && e < a.E) my_rank = e / er;
     }
+    if (lane < a.R) {
+        const int32_t rs = a.rank_slot[t * a.R + lane];
+        if (rs >= 0 && rs < a.recv_rows) my_rs = rs;
+    }
 #pragma unroll
-    for (int k = 0; k < KMAX; ++k) ranks[k] = readlane(my_rank, k);
+    for (int k = 0; k < KMAX; ++k) {
+        d.rows[k] = readlane(my_row, k);
+        d.w[k] = readlane(my_w, k);
+        d.ranks[k] = readlane(my_rank, k);
+    }
+    d.my_rs = my_rs;
 }
 
 // Sum of the weights of the token's contributing entries, per rank then across
 // ranks in ascending order (the grouping of the dedup combine).
 template <int KMAX>
-__device__ __forceinline__ float dedup_weight_sum(const CombineArgs& a, int64_t t,
-                                                  const int (&rows)[KMAX], const int (&ranks)[KMAX],
-                                                  const float (&w)[KMAX]) {
+__device__ __forceinline__ float dedup_weight_sum(const CombineArgs& a, const DedupToken<KMAX>& d) {
     float s = 0.0f;
     for (int r = 0; r < a.R; ++r) {
-        const int32_t rs = a.rank_slot[t * a.R + r];
-        if (rs < 0 || rs >= a.recv_rows) continue;
+        if (d.recv_row(r) < 0) continue;
         float pw = 0.0f;
 #pragma unroll
         for (int k = 0; k < KMAX; ++k)
-            if (rows[k] >= 0 && ranks[k] == r) pw = pw + w[k];
+            if (d.rows[k] >= 0 && d.ranks[k] == r) pw = pw + d.w[k];
         s = s + pw;
     }
     return s;
@@ -295,32 +328,36 @@ template <bool YF32, bool OF32, int KMAX, int MODE>
 __device__ __forceinline__ void dedup_item(const CombineArgs& a, int64_t t, int c, int C) {
     const int64_t H = a.H;
     const int units = (int)(H / 8);
-    int rows[KMAX], ranks[KMAX];
-    float w[KMAX];
-    token_entries<KMAX>(a, t, rows, w);
-    entry_ranks<KMAX>(a, t, ranks);
+    DedupToken<KMAX> d;
+    dedup_token<KMAX>(a, t, d);
 
     const int u = c * C + (int)threadIdx.x;
     if ((int)threadIdx.x < C && u < units) {
         Unit<YF32> y[KMAX];
 #pragma unroll
-        for (int k = 0; k < KMAX; ++k)
-            if (rows[k] >= 0) y[k].load(a.y, rows[k], H, (int64_t)u * 8);
+        for (int k = 0; k < KMAX; ++k) {
+            y[k].clear();
+            if (d.rows[k] >= 0) y[k].load(a.y, d.rows[k], H, (int64_t)u * 8);
+        }
+        // one wait for all K rows: the per-rank loop below uses them under
+        // conditions and, in the two-stage form, stores between the uses
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) y[k].settle();
         float acc[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
         for (int r = 0; r < a.R; ++r) {
-            const int32_t rs = a.rank_slot[t * a.R + r];
-            if (rs < 0 || rs >= a.recv_rows) continue;
+            const int rs = d.recv_row(r);
+            if (rs < 0) continue;
             float p[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) p[j] = 0.0f;
 #pragma unroll
             for (int k = 0; k < KMAX; ++k) {
-                if (rows[k] < 0 || ranks[k] != r) continue;
+                if (d.rows[k] < 0 || d.ranks[k] != r) continue;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    const float prod = w[k] * y[k].get(j);
+                    const float prod = d.w[k] * y[k].get(j);
                     p[j] = p[j] + prod;
                 }
             }
@@ -334,7 +371,7 @@ __device__ __forceinline__ void dedup_item(const CombineArgs& a, int64_t t, int 
         if (MODE == 0) store_unit<OF32>(a.out, t, H, (int64_t)u * 8, acc);
     }
     if (MODE == 0 && c == 0 && threadIdx.x == 0 && a.out_weights)
-        a.out_weights[t] = dedup_weight_sum<KMAX>(a, t, rows, ranks, w);
+        a.out_weights[t] = dedup_weight_sum<KMAX>(a, d);
 }
 
 template <bool YF32, bool OF32, int KMAX, int MODE>
@@ -346,33 +383,43 @@ __global__ __launch_bounds__(kCombThreads) void dedup_combine_kernel(CombineArgs
     }
 }
 
-// stage B: out[t] = 0 + partial[rank_slot[t][r]] for r ascending
+// stage B: out[t] = 0 + partial[rank_slot[t][r]] for r ascending.  The partial
+// rows of up to kSumBatch ranks are loaded together, then added in rank order.
+constexpr int kSumBatch = 8;
+
 template <bool OF32, int KMAX>
 __device__ __forceinline__ void dedup_sum_item(const CombineArgs& a, int64_t t, int c, int C) {
     const int64_t H = a.H;
     const int units = (int)(H / 8);
+    DedupToken<KMAX> d;
+    dedup_token<KMAX>(a, t, d);
     const int u = c * C + (int)threadIdx.x;
     if ((int)threadIdx.x < C && u < units) {
         float acc[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
-        for (int r = 0; r < a.R; ++r) {
-            const int32_t rs = a.rank_slot[t * a.R + r];
-            if (rs < 0 || rs >= a.recv_rows) continue;
-            Unit<true> p;
-            p.load(a.partial, rs, H, (int64_t)u * 8);
+        for (int r0 = 0; r0 < a.R; r0 += kSumBatch) {
+            Unit<true> p[kSumBatch];
+            int rs[kSumBatch];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) acc[j] = acc[j] + p.get(j);
+            for (int i = 0; i < kSumBatch; ++i) {
+                rs[i] = r0 + i < a.R ? d.recv_row(r0 + i) : -1;
+                p[i].clear();
+                if (rs[i] >= 0) p[i].load(a.partial, rs[i], H, (int64_t)u * 8);
+            }
+            // one wait for the batch instead of one per conditional use
+#pragma unroll
+            for (int i = 0; i < kSumBatch; ++i) p[i].settle();
+#pragma unroll
+            for (int i = 0; i < kSumBatch; ++i) {
+                if (rs[i] < 0) continue;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc[j] = acc[j] + p[i].get(j);
+            }
         }
         store_unit<OF32>(a.out, t, H, (int64_t)u * 8, acc);
     }
-    if (c == 0 && a.out_weights) {
-        int rows[KMAX], ranks[KMAX];
-        float w[KMAX];
-        token_entries<KMAX>(a, t, rows, w);
-        entry_ranks<KMAX>(a, t, ranks);
-        if (threadIdx.x == 0) a.out_weights[t] = dedup_weight_sum<KMAX>(a, t, rows, ranks, w);
-    }
+    if (c == 0 && threadIdx.x == 0 && a.out_weights) a.out_weights[t] = dedup_weight_sum<KMAX>(a, d);
 }
 
 template <bool OF32, int KMAX>
@@ -423,6 +470,7 @@ void by_k(const CombineArgs& a, hipStream_t s) {
     }
     MOE_K_CASE(2)
     MOE_K_CASE(4)
+    if (dd) MOE_K_CASE(6)   // the dedup forms hold K f32 rows per lane: fewer registers at K=6
     MOE_K_CASE(8)
     MOE_K_CASE(16)
 #undef MOE_K_CASE

@@ -193,6 +193,12 @@ __device__ __forceinline__ void recv_copy_kernel_item(const RecvArgs& a, int64_t
 // dedup stage 2: each recv row of token t expanded to the token's entries on
 // that rank (the same slots a plain dispatch of the surviving ids gives)
 // ---------------------------------------------------------------------------
+// Ranks are taken in ascending order in batches of kRankBatch: the recv rows of
+// a batch are loaded together (one memory round trip per batch instead of per
+// rank), then copied to the token's entries on each rank.  The ranks that have
+// a recv row and an entry form a wave-uniform bit mask, walked lowest bit first.
+constexpr int kRankBatch = 2;
+
 template <int KMAX, int VPT>
 __device__ __forceinline__ void expand_kernel_item(const ExpandArgs& a, int64_t t, int nth) {
     const int tid = threadIdx.x;
@@ -203,7 +209,8 @@ __device__ __forceinline__ void expand_kernel_item(const ExpandArgs& a, int64_t 
     const int64_t row_bytes = a.H * a.x_bytes;
     const int nvec = (int)(row_bytes / 16);
 
-    int my_row = -1, my_rank = -1;
+    int my_rs = -1, my_row = -1, my_rank = -1;
+    if (lane < R) my_rs = a.rank_slot[t * R + lane];
     if (lane < K) {
         const int64_t f = t * K + lane;
         my_row = entry_row(a.slot, f);
@@ -216,32 +223,48 @@ __device__ __forceinline__ void expand_kernel_item(const ExpandArgs& a, int64_t 
     int rows[KMAX], ranks[KMAX];
     broadcast_rows<KMAX>(my_row, rows);
     broadcast_rows<KMAX>(my_rank, ranks);
+    bool has = false;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) has |= (k < K) && rows[k] >= 0 && ranks[k] == lane;
+    const uint64_t todo = ballot64(lane < R && my_rs >= 0 && has);
 
-    for (int r = 0; r < R; ++r) {
-        bool any = false;
+    for (int base = 0; base < nvec; base += VPT * nth) {
+        uint64_t mask = todo;
+        while (mask) {
+            int rk[kRankBatch], srow[kRankBatch];
+            u32x4 val[kRankBatch][VPT];
 #pragma unroll
-        for (int k = 0; k < KMAX; ++k) any |= (k < K) && ranks[k] == r && rows[k] >= 0;
-        if (!any) continue;
-        const int32_t srow = a.rank_slot[t * R + r];
-        const char* src = (const char*)a.recv_x + (int64_t)srow * row_bytes;
-        for (int base = 0; base < nvec; base += VPT * nth) {
-            u32x4 val[VPT];
-#pragma unroll
-            for (int i = 0; i < VPT; ++i) {
-                const int v = base + tid + i * nth;
-                val[i] = u32x4{0, 0, 0, 0};
-                if (v < nvec) val[i] = ld16_stream(src + (int64_t)v * 16);
-            }
-            settle(val);
-#pragma unroll
-            for (int k = 0; k < KMAX; ++k) {
-                if (k >= K) break;
-                if (ranks[k] != r || rows[k] < 0) continue;
-                char* out = (char*)a.packed + (int64_t)rows[k] * row_bytes;
+            for (int b = 0; b < kRankBatch; ++b) {
+                rk[b] = -1;
+                srow[b] = -1;
+                if (mask) {
+                    rk[b] = __builtin_ctzll(mask);
+                    mask &= mask - 1;
+                    srow[b] = readlane(my_rs, rk[b]);
+                }
+                const char* src = (const char*)a.recv_x + (int64_t)srow[b] * row_bytes;
 #pragma unroll
                 for (int i = 0; i < VPT; ++i) {
                     const int v = base + tid + i * nth;
-                    if (v < nvec) st16(out + (int64_t)v * 16, val[i]);
+                    val[b][i] = u32x4{0, 0, 0, 0};
+                    if (rk[b] >= 0 && v < nvec) val[b][i] = ld16_stream(src + (int64_t)v * 16);
+                }
+            }
+#pragma unroll
+            for (int b = 0; b < kRankBatch; ++b) settle(val[b]);
+#pragma unroll
+            for (int b = 0; b < kRankBatch; ++b) {
+                if (rk[b] < 0) continue;
+#pragma unroll
+                for (int k = 0; k < KMAX; ++k) {
+                    if (k >= K) break;
+                    if (ranks[k] != rk[b] || rows[k] < 0) continue;
+                    char* out = (char*)a.packed + (int64_t)rows[k] * row_bytes;
+#pragma unroll
+                    for (int i = 0; i < VPT; ++i) {
+                        const int v = base + tid + i * nth;
+                        if (v < nvec) st16_stream(out + (int64_t)v * 16, val[b][i]);
+                    }
                 }
             }
         }

@@ -325,6 +325,33 @@ def test_dedup_small(case):
             np.testing.assert_array_equal(host(part)[:n].view(np.uint32), ep[:n].view(np.uint32))
 
 
+@pytest.mark.parametrize("K,E,R,H", [(2, 16, 4, 256), (4, 64, 32, 128), (5, 40, 8, 512),
+                                     (8, 64, 8, 384), (12, 96, 16, 256), (16, 64, 32, 128)])
+def test_dedup_shapes(K, E, R, H):
+    """Every entry-count instantiation and rank counts up to 32 (several rank
+    batches per token in the expansion and the partial sums)."""
+    rng = np.random.default_rng(K * 31 + R)
+    T = 700
+    idx = _mixed_idx(rng, T, K, E)
+    x = W.normal_x(rng, T, H, "f32")
+    w = rng.random((T, K)).astype(np.float32)
+    note(f"dedup shapes K={K} E={E} R={R} H={H}")
+    o = _gpu_dedup(dev(x), idx, E, R)
+    ref = oracle.dedup_dispatch(x, "f32", idx, E, R)
+    _assert_dedup_equal(o, ref)
+    rr = T * min(K, R)
+    for with_partial in (True, False):
+        part = torch.empty((rr, H), dtype=torch.float32, device=DEV) if with_partial else None
+        poison_(part)
+        plan = dict(R=R, idx=dev(idx), rank_slot=o.rank_slot, recv_rows=rr, partial=part)
+        out, ow = moe.combine(o.packed, o.tok_map, dev(w), E=E, out_dtype=torch.float32, dedup=plan)
+        torch.cuda.synchronize()
+        eo, ew, _ = oracle.dedup_combine(ref["packed"], "f32", ref["tok_map"], w, idx, E, R,
+                                         ref["rank_slot"], rr, "f32")
+        _check_combine(host(out), eo, "f32")
+        np.testing.assert_array_equal(host(ow), ew)
+
+
 def test_dedup_workload_full():
     d = W.make_inputs("dedup")
     E, R, K, T, H = d["E"], d["R"], d["K"], d["T"], d["H"]
