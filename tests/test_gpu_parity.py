@@ -751,3 +751,63 @@ def test_fp4_end_to_end_skewed_full():
     np.testing.assert_array_equal(host(ow), ew)
     assert torch.equal(packed, o.packed) and torch.equal(scales.view(torch.int32), o.scales.view(torch.int32))
 
+
+# ---------------------------------------------------------------------------
+# edge cases of the quantized and replay entry points
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("case", ["T0", "rows0", "K16_E1024", "all_neg", "H128"])
+@pytest.mark.parametrize("payload", ["fp8", "fp4", "prequant"])
+def test_quantized_dispatch_edges(case, payload):
+    rng = np.random.default_rng(6)
+    T, K, E, H, rows = 40, 4, 16, 256, None
+    if case == "T0":
+        T = 0
+    elif case == "K16_E1024":
+        K, E, T = 16, 1024, 300
+    elif case == "H128":
+        H = 128
+    idx = rng.integers(-1, E, size=(T, K)).astype(np.int32)
+    if case == "all_neg":
+        idx[:] = -1
+    if case == "rows0":
+        rows = 0
+    note(f"quantized dispatch edge {case} {payload}")
+    if rows is None:
+        rows = T * K
+    if payload == "prequant":
+        q = rng.integers(0, 256, size=(T, H), dtype=np.uint8)
+        sc = (rng.random((T, H // 128)) + 0.5).astype(np.float32)
+        o = moe._lib.alloc_dispatch(T, H, K, E, rows, torch.uint8, True, DEV)
+        for t in (o.packed, o.scales, o.packed_src, o.tok_map, o.packed_cnt, o.packed_off, o.stats):
+            poison_(t)
+        qd = dev(q) if T else torch.empty((0, H), dtype=torch.uint8, device=DEV)
+        sd = dev(sc) if T else torch.empty((0, H // 128), dtype=torch.float32, device=DEV)
+        moe.dispatch_prequant(qd, sd, dev(idx) if T else torch.empty((0, K), dtype=torch.int32, device=DEV),
+                              E, packed_rows=rows, out=o)
+        torch.cuda.synchronize()
+        ref = oracle.dispatch(q, "fp8", idx, E, packed_rows=rows, x_scales=sc)
+    else:
+        x = W.normal_x(rng, T, H, "bf16")
+        xd = dev_bf16(x) if T else torch.empty((0, H), dtype=torch.bfloat16, device=DEV)
+        o = gpu_dispatch(xd, idx, E, packed_rows=rows, fp8=payload == "fp8", fp4=payload == "fp4")
+        ref = oracle.dispatch(x, "bf16", idx, E, packed_rows=rows, packed_dt=payload)
+    assert_dispatch_equal(o, ref, fp8=True)
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "fp4"])
+def test_quantized_combine_and_replay_empty(fmt):
+    """T = 0 and zero rows are no-ops that return OK."""
+    H, K = 128, 4
+    width = H // 2 if fmt == "fp4" else H
+    q = torch.empty((0, width), dtype=torch.uint8, device=DEV)
+    tm = torch.empty((0, K), dtype=torch.int64, device=DEV)
+    w = torch.empty((0, K), dtype=torch.float32, device=DEV)
+    fn = moe.combine_fp4 if fmt == "fp4" else moe.combine_fp8
+    out, ow = fn(q, None, tm, w)
+    x = torch.empty((0, H), dtype=torch.bfloat16, device=DEV)
+    moe.dispatch_replay(x, tm, torch.empty((0, width), dtype=torch.uint8, device=DEV),
+                        scales=torch.empty((0, 1), dtype=torch.float32, device=DEV), fp4=fmt == "fp4")
+    torch.cuda.synchronize()
+    assert out.shape == (0, H) and ow.shape == (0,)
+
