@@ -227,11 +227,22 @@ __device__ __forceinline__ void combine_fp8_item(const CombineArgs& a, int64_t t
                     unpack_e4m3x2<true>(code[k][d], v[4 * d + 2], v[4 * d + 3]);
                 }
             }
+            // v * 1.0f == v bitwise, so when every lane's block scale of this row
+            // is 1 (all unscaled blocks) the dequantize multiply is skipped; the
+            // VALU, not HBM, is what the quantized forms run short of
+            if (ballot64(scl[k] != 1.0f) == 0) {
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const float dq = v[j] * scl[k];
-                const float p = w[k] * dq;
-                acc[j] = acc[j] + p;
+                for (int j = 0; j < 16; ++j) {
+                    const float p = w[k] * v[j];
+                    acc[j] = acc[j] + p;
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const float dq = v[j] * scl[k];
+                    const float p = w[k] * dq;
+                    acc[j] = acc[j] + p;
+                }
             }
         }
         float lo[8], hi[8];
