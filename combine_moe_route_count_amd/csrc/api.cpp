@@ -3,8 +3,6 @@
 // first launch, so a call that returns an error has enqueued nothing.
 #include <hip/hip_runtime_api.h>
 
-#include <atomic>
-#include <chrono>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -150,21 +148,6 @@ struct LevelOut {
     int32_t* stats = nullptr;
 };
 
-// A distinct nonzero tag per one-launch routing call, seeded from the clock so
-// a ticket left in a reused workspace by an earlier process cannot match.
-uint32_t next_epoch() {
-    static std::atomic<uint32_t> counter{(uint32_t)std::chrono::steady_clock::now()
-                                             .time_since_epoch()
-                                             .count() |
-                                         1u};
-    // A tag of four equal bytes could match a workspace filled by a byte memset.
-    uint32_t e;
-    do {
-        e = counter.fetch_add(1, std::memory_order_relaxed);
-    } while (e == (e & 0xFFu) * 0x01010101u);
-    return e;
-}
-
 hipError_t route_level(void* ws, const RouteWs& L, size_t ticket, moe::KeyKind kind,
                        const int32_t* idx, const int32_t* rank_slot, int64_t N, int K, int E,
                        int R, int NK, int64_t cap, int64_t rows_limit, const LevelOut& o,
@@ -198,7 +181,6 @@ hipError_t route_level(void* ws, const RouteWs& L, size_t ticket, moe::KeyKind k
         fa.local_rank = at<int32_t>(ws, L.local_rank);
         fa.scan = sa;
         fa.ticket = at<uint64_t>(ws, ticket);
-        fa.epoch = next_epoch();
         return moe::launch_route_fused(fa, s);
     }
     moe::RankArgs ra;

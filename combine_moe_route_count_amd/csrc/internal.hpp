@@ -123,8 +123,7 @@ struct RouteFusedArgs {
     int nbits;          // key bits of NK
     int32_t* local_rank;
     ScanArgs scan;      // tiles, NK, tile counts in the workspace, outputs
-    uint64_t* ticket;   // in the workspace: (epoch << 32) | tiles finished
-    uint32_t epoch;     // distinct per call, never 0
+    uint64_t* ticket;   // in the workspace: (tag << 32) | tiles finished
 };
 hipError_t launch_route_fused(const RouteFusedArgs& a, hipStream_t s);
 

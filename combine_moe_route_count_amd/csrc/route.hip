@@ -43,7 +43,7 @@ __global__ __launch_bounds__(kRankThreads) void rank_tiles_kernel(
 }
 
 __global__ __launch_bounds__(kScanThreads) void scan_tiles_kernel(ScanArgs a) {
-    scan_tiles_body(a);
+    scan_tiles_body<false>(a);
 }
 
 }  // namespace

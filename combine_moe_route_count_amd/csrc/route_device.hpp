@@ -165,6 +165,13 @@ __device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t* wave
 // loads their counts once (all loads issued together), sums them, takes the
 // prefix of the earlier parts from LDS and writes the exclusive tile bases.
 // The per-key totals are then scanned over keys for the offsets.
+template <bool COHERENT>
+__device__ __forceinline__ int32_t ld_count(const int32_t* p) {
+    if (COHERENT) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return *p;
+}
+
+template <bool COHERENT>
 __device__ __forceinline__ void scan_tiles_body(const ScanArgs& a) {
     __shared__ int32_t part_sum[kScanThreads];
     __shared__ int32_t key_total[kScanThreads];
@@ -189,17 +196,18 @@ __device__ __forceinline__ void scan_tiles_body(const ScanArgs& a) {
 #pragma unroll
     for (int i = 0; i < kScanCache; ++i) {
         const int tl = t0 + i;
-        c[i] = (active && tl < t1) ? a.tile_cnt[(int64_t)tl * NK + key] : 0;
+        c[i] = (active && tl < t1) ? ld_count<COHERENT>(&a.tile_cnt[(int64_t)tl * NK + key]) : 0;
     }
     int32_t fi = 0, fd = 0;
     for (int tl = tid; tl < tiles; tl += kScanThreads) {
-        fi += a.tile_flags[2 * (int64_t)tl];
-        fd += a.tile_flags[2 * (int64_t)tl + 1];
+        fi += ld_count<COHERENT>(&a.tile_flags[2 * (int64_t)tl]);
+        fd += ld_count<COHERENT>(&a.tile_flags[2 * (int64_t)tl + 1]);
     }
 #pragma unroll
     for (int i = 0; i < kScanCache; ++i) s += c[i];
     if (active)
-        for (int tl = t0 + kScanCache; tl < t1; ++tl) s += a.tile_cnt[(int64_t)tl * NK + key];
+        for (int tl = t0 + kScanCache; tl < t1; ++tl)
+            s += ld_count<COHERENT>(&a.tile_cnt[(int64_t)tl * NK + key]);
     if (tid == 0) {
         red[0] = 0;
         red[1] = 0;
@@ -222,7 +230,7 @@ __device__ __forceinline__ void scan_tiles_body(const ScanArgs& a) {
         }
         for (int tl = t0 + kScanCache; tl < t1; ++tl) {
             const int64_t j = (int64_t)tl * NK + key;
-            const int32_t cc = a.tile_cnt[j];
+            const int32_t cc = ld_count<COHERENT>(&a.tile_cnt[j]);
             a.tile_cnt[j] = run;
             run += cc;
         }

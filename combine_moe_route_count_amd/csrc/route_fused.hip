@@ -19,33 +19,33 @@ namespace moe {
 namespace {
 
 constexpr int kFusedThreads = 1024;
+constexpr uint32_t kTicketTag = 0x5A17C0DEu;   // no byte-repeat pattern a memset could leave
 constexpr int kFusedWaves = kFusedThreads / kWave;
 
-// Arrival on the epoch-tagged ticket; returns this launch's count after the
-// arrival.  A stored epoch that differs (an earlier launch, a cleared ticket,
-// or whatever an uninitialised workspace holds) is replaced by (epoch, 1) with
-// one compare-and-swap; once the word carries this launch's epoch, arrivals
-// are plain fetch-adds, which the atomic unit serves back to back instead of
-// failing and retrying under contention.  The epoch cannot change under an
-// arrival: only the last arrival of this launch clears the word.
-__device__ uint32_t arrive_ticket(uint64_t* ticket, uint32_t epoch) {
+// Arrival on the tagged ticket; returns this launch's count after the arrival.
+// The word holds (kTicketTag << 32) | arrivals; the last arrival of every
+// launch re-arms it to (kTicketTag << 32) | 0, so each launch after a completed
+// one arrives with a single fetch-add.  A word that does not carry the tag
+// (a workspace never used, or reused for something else) is repaired once:
+// arrivals that find it stale replace it by (tag, 1) with a compare-and-swap,
+// or, once another arrival has done so, fetch-add like everyone else; the
+// adds that hit the stale word are discarded with it.
+__device__ uint32_t arrive_ticket(uint64_t* ticket) {
+    const uint64_t old =
+        __hip_atomic_fetch_add(ticket, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((uint32_t)(old >> 32) == kTicketTag) return (uint32_t)old + 1u;
     uint64_t cur = __hip_atomic_load(ticket, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if ((uint32_t)(cur >> 32) != epoch) {
-        const uint64_t fresh = ((uint64_t)epoch << 32) | 1ull;
+    const uint64_t fresh = ((uint64_t)kTicketTag << 32) | 1ull;
+    for (;;) {
+        if ((uint32_t)(cur >> 32) == kTicketTag) {
+            const uint64_t o =
+                __hip_atomic_fetch_add(ticket, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return (uint32_t)o + 1u;
+        }
         if (__hip_atomic_compare_exchange_strong(ticket, &cur, fresh, __ATOMIC_RELAXED,
                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
             return 1u;
-        // cur now holds the word that beat us; it is either this launch's
-        // (an arrival got there first) or still stale, in which case retry.
-        while ((uint32_t)(cur >> 32) != epoch) {
-            if (__hip_atomic_compare_exchange_strong(ticket, &cur, fresh, __ATOMIC_RELAXED,
-                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
-                return 1u;
-        }
     }
-    const uint64_t old =
-        __hip_atomic_fetch_add(ticket, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return (uint32_t)old + 1u;
 }
 
 template <class KeyFn>
@@ -62,12 +62,16 @@ __global__ __launch_bounds__(kFusedThreads) void route_fused_kernel(KeyFn keys, 
     // kernel's streaming stores fill, and measured about 10 us per launch.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (tid == 0) s_last = arrive_ticket(a.ticket, a.epoch) == (uint32_t)a.scan.tiles;
+    if (tid == 0) s_last = arrive_ticket(a.ticket) == (uint32_t)a.scan.tiles;
     __syncthreads();
     if (!s_last) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // every tile's counts visible
-    scan_tiles_body(a.scan);
-    if (tid == 0) __hip_atomic_store(a.ticket, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // Every tile's counts are at the coherence point (agent-scope stores that
+    // completed before their ticket arrivals, which precede this one); the scan
+    // reads them with agent-scope loads, so no cache invalidate is needed.
+    scan_tiles_body<true>(a.scan);
+    if (tid == 0)
+        __hip_atomic_store(a.ticket, (uint64_t)kTicketTag << 32, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace

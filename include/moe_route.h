@@ -87,7 +87,9 @@ const char* moe_last_error(void);
  * R > 0) moe_dedup_dispatch need for these sizes.  The workspace needs no
  * initialisation and may be reused by consecutive calls on one stream, also
  * from a captured graph.  Calls that may run at the same time (other streams)
- * need workspaces of their own: the routing keeps an arrival counter in it. */
+ * need workspaces of their own: the routing keeps an arrival counter in it,
+ * which every completed call leaves re-armed.  After a call that did not run to
+ * completion (a device error), clear the workspace before using it again. */
 size_t moe_workspace_size(int64_t T, int K, int E, int R);
 
 /* Routing histogram and exclusive scan ("cco + flydsl dispatch/combine",
