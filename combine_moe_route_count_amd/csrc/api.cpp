@@ -216,7 +216,7 @@ moe::SlotArgs slot_args(void* ws, const RouteWs& L, const int32_t* idx, int K, i
 
 }  // namespace
 
-MOE_API int moe_version(void) { return (1 << 16) | 0; }
+MOE_API int moe_version(void) { return (1 << 16) | 1; }
 
 MOE_API const char* moe_last_error(void) { return g_last_error.c_str(); }
 

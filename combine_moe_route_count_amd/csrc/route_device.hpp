@@ -161,16 +161,20 @@ __device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t* wave
     return before + x - v;
 }
 
-// One workgroup of kScanThreads threads.  Thread (key, part) owns the tiles [t0, t1) of one key: it
-// loads their counts once (all loads issued together), sums them, takes the
-// prefix of the earlier parts from LDS and writes the exclusive tile bases.
-// The per-key totals are then scanned over keys for the offsets.
+// A published tile count.  COHERENT: read at agent scope, for counts that
+// other workgroups of the same launch stored at agent scope (the one-launch
+// routing); otherwise a plain load (counts from an earlier kernel).
 template <bool COHERENT>
 __device__ __forceinline__ int32_t ld_count(const int32_t* p) {
     if (COHERENT) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return *p;
 }
 
+// One workgroup of kScanThreads threads.  Thread (key, part) owns the tiles
+// [t0, t1) of one key: it loads their counts once (all loads issued together),
+// sums them, takes the prefix of the earlier parts from LDS and writes the
+// exclusive tile bases.  The per-key totals are then scanned over keys for the
+// offsets.
 template <bool COHERENT>
 __device__ __forceinline__ void scan_tiles_body(const ScanArgs& a) {
     __shared__ int32_t part_sum[kScanThreads];

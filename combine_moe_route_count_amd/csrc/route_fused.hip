@@ -2,9 +2,9 @@
 // then the tile / key scan run by whichever routing workgroup finishes last.
 //
 // Workgroups of 1024 threads each rank one tile of 1024 entries (16 waves x one
-// 64-entry chunk, the pass of route.hip), write back their counts, and take a
-// ticket.  The workgroup that takes the last ticket runs the scan of
-// route.hip on everyone's counts and clears the ticket.  Nobody waits for
+// 64-entry chunk, the pass of route.hip), publish their counts with agent-scope
+// stores, and take a ticket.  The workgroup that takes the last ticket runs the
+// scan of route.hip on everyone's counts and re-arms the ticket.  Nobody waits for
 // anybody: a workgroup either finishes after its tile or, being last, after the
 // scan, so the launch needs no co-residency and cannot hang (the CTA-local rule
 // of "Drop cooperative launch from the CTA-independent local kernels", MoonEP

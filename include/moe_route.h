@@ -13,7 +13,12 @@
  *   - out_weights (commit "Combine now reduces the K forwarded per-token
  *     weight vectors into out_weights"): the sum of the valid weights;
  *   - Fp8BlockwiseQuant (commit "Port mori's Fp8BlockwiseQuant ..."): one f32
- *     scale per 128-element block, OCP e4m3 payload;
+ *     scale per 128-element block, OCP e4m3 payload, dequantized inside the
+ *     combine's reduction on the receiving side;
+ *   - the fp4 e2m1 accumulator path (commit "Add the fp4 e2m1 accum path ..."):
+ *     8 codes per 32-bit word, hidden/2 bytes per row;
+ *   - replay dispatch and forwarded quant scales (commit "... routing handle,
+ *     LEC, reset, replay"): a cached tok_map reused with the identical layout;
  *   - the dispatch dedup (PR description, "ballot dedup"; and "Drop
  *     cooperative launch from the CTA-independent local kernels", MoonEP pull
  *     34, "Why it's worth doing": one copy per dedup group, expanded locally,
@@ -32,8 +37,10 @@
  * Layouts are row-major.  Expert ids are int32 [T,K]; id e is valid iff
  * 0 <= e < E; -1 means "no expert" and is skipped silently; any other value is
  * skipped and counted as invalid.  Row data: bf16 (uint16 bit patterns) or
- * f32, H elements per row; packed fp8 rows hold H OCP e4m3fn bytes with one
- * f32 scale per 128-element block in a separate [rows, H/128] array.
+ * f32, H elements per row; packed fp8 rows hold H OCP e4m3fn bytes and packed
+ * fp4 rows H/2 bytes of OCP e2m1 codes (element 2i in the low nibble of byte
+ * i), each with one f32 scale per 128-element block in a separate
+ * [rows, H/128] array.
  *
  * Slots.  Within an expert, entries take consecutive slots in flat order
  * f = t*K + k.  With cap > 0 (padded layout) expert e owns rows
@@ -54,7 +61,7 @@
  * last error.
  *
  * Limits: 0 <= T, 1 <= K <= 16, 1 <= E <= 1024, T*K < 2^31, H > 0 with
- * H % 8 == 0 (H % 128 == 0 for fp8), packed_rows and recv_rows <= 2^31-1,
+ * H % 8 == 0 (H % 128 == 0 for fp8 and fp4), packed_rows and recv_rows <= 2^31-1,
  * row pointers 16-byte aligned, 1 <= R <= 32 with E % R == 0.
  */
 #ifndef MOE_ROUTE_H
@@ -83,8 +90,9 @@ int moe_version(void);
 /* Text of the calling thread's last non-OK status ("" if none). */
 const char* moe_last_error(void);
 
-/* Bytes of device workspace that moe_route_count, moe_dispatch and (with
- * R > 0) moe_dedup_dispatch need for these sizes.  The workspace needs no
+/* Bytes of device workspace that moe_route_count, moe_dispatch,
+ * moe_dispatch_prequant and (with R > 0) moe_dedup_dispatch need for these
+ * sizes (moe_dispatch_replay and the combines need none).  The workspace needs no
  * initialisation and may be reused by consecutive calls on one stream, also
  * from a captured graph.  Calls that may run at the same time (other streams)
  * need workspaces of their own: the routing keeps an arrival counter in it,
@@ -104,7 +112,8 @@ int moe_route_count(const int32_t* idx, int64_t T, int K, int E, int32_t* cnt, i
 
 /* Dispatch: count, scan, assign slots and scatter rows into per-expert packed
  * buffers (convert_dispatch_output), optionally packing bf16 to blockwise fp8.
- *   x            [T,H] x_dt (MOE_BF16 or MOE_F32)
+ *   x            [T,H] x_dt (MOE_BF16 or MOE_F32; fp8 input goes through
+ *                moe_dispatch_prequant, which also takes its scales)
  *   cap          > 0: padded layout, rows [e*cap, e*cap+cap); 0: compact layout
  *   packed_rows  rows of packed_x (and packed_src, packed_scales)
  *   packed_x     out [packed_rows,H] packed_dt: x_dt, or MOE_FP8_E4M3 / MOE_FP4_E2M1
@@ -146,7 +155,7 @@ int moe_dispatch_prequant(const uint8_t* x_q, const float* x_scales, int64_t T, 
 /* Replay dispatch (same page and commit: the replay reuses the cached tok_map
  * with the identical layout): no counting, scan or slotting; for every entry
  * with 0 <= tok_map[t,k] < packed_rows, row tok_map[t,k] of packed_x receives
- * token t exactly as moe_dispatch (bf16/f32 bit copy, bf16 -> fp8 pack) or
+ * token t exactly as moe_dispatch (bf16/f32 bit copy, bf16 -> fp8 or fp4 pack) or
  * moe_dispatch_prequant (fp8 codes plus the scale row) would write it.
  * Nothing else is written: packed_src, packed_cnt and the routing stay as the
  * earlier dispatch left them.  tok_map must hold each row at most once (any
@@ -181,7 +190,8 @@ typedef struct moe_dedup_plan {
 /* Combine: weighted gather-reduce back to token order (convert_combine_input
  * and the f32 gather), plus out_weights.
  *   y            [y_rows,H] y_dt (MOE_BF16 or MOE_F32), the expert outputs in
- *                packed-row order
+ *                packed-row order (fp8 / fp4 outputs: moe_combine_fp8 /
+ *                moe_combine_fp4; y_dt MOE_FP8_E4M3 here is MOE_ERR_UNSUPPORTED)
  *   tok_map      int64 [T,K] from the dispatch; rows outside [0,y_rows) are skipped
  *   w            f32 [T,K] gate weights
  *   dd           NULL: acc = 0, then for k ascending acc = acc + (w * y[row]),
