@@ -153,4 +153,26 @@ __device__ __forceinline__ void st8_stream(void* p, u32x2 v) {
     __builtin_nontemporal_store(v, (u32x2*)p);
 }
 
+// A destination row addressed through a buffer resource.  The row base is
+// wave-uniform (a broadcast row index), so it stays in scalar registers and
+// each lane adds only its byte offset; an offset outside the row is dropped by
+// the hardware range check.  Stores carry the agent-scope streaming policy
+// (sc1 nt): written through L2 as data that is not read again soon.  On the
+// write-heavy dispatch this measured about 3% faster than the plain
+// non-temporal store (which keeps the line in L2 until eviction); on the
+// read-heavy combine the two were equal.
+constexpr int kStoreThrough = (1 << 4) | (1 << 1);  // cache policy bits: sc1, nt
+constexpr int kRsrcWord3 = 0x00020000;               // gfx9 descriptor word 3: 32-bit raw data
+struct RowOut {
+    __amdgpu_buffer_rsrc_t r;
+    __device__ __forceinline__ RowOut(void* row, int64_t bytes)
+        : r(__builtin_amdgcn_make_buffer_rsrc(row, 0, (int)bytes, kRsrcWord3)) {}
+    __device__ __forceinline__ void st16(int off, u32x4 v) const {
+        __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kStoreThrough);
+    }
+    __device__ __forceinline__ void st8(int off, u32x2 v) const {
+        __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kStoreThrough);
+    }
+};
+
 }  // namespace moe

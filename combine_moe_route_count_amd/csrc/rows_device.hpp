@@ -55,11 +55,11 @@ __device__ __forceinline__ void store_row_copies(const char* src, int nvec, char
         for (int d = 0; d < DMAX; ++d) {
             if (d >= D) break;
             if (rows[d] < 0) continue;
-            char* out = dst + (int64_t)rows[d] * row_bytes;
+            const RowOut out(dst + (int64_t)rows[d] * row_bytes, row_bytes);
 #pragma unroll
             for (int i = 0; i < VPT; ++i) {
                 const int v = base + tid + i * nthreads;
-                if (v < nvec) st16_stream(out + (int64_t)v * 16, val[i]);
+                if (v < nvec) out.st16(v * 16, val[i]);
             }
         }
         base += step;

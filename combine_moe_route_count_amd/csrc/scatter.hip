@@ -129,14 +129,14 @@ __device__ __forceinline__ void scatter_fp8_kernel_item(const ScatterArgs& a, in
         for (int d = 0; d < DMAX; ++d) {
             if (d >= K) break;
             if (rows[d] < 0) continue;
-            char* out = (char*)a.packed + (int64_t)rows[d] * prow;
+            const RowOut out((char*)a.packed + (int64_t)rows[d] * prow, prow);
             float* sc = a.scales + (int64_t)rows[d] * nblk;
 #pragma unroll
             for (int i = 0; i < UPT; ++i) {
                 const int u = base + tid + i * nth;
                 if (u < nunits) {
-                    if (FP4) st8_stream(out + (int64_t)u * 8, q4[i]);
-                    else st16_stream(out + (int64_t)u * 16, q[i]);
+                    if (FP4) out.st8(u * 8, q4[i]);
+                    else out.st16(u * 16, q[i]);
                     if ((u & 7) == 0) sc[u >> 3] = s[i];  // cached: L2 merges the 32-byte pieces of a scale row
                 }
             }
@@ -259,11 +259,11 @@ __device__ __forceinline__ void expand_kernel_item(const ExpandArgs& a, int64_t 
                 for (int k = 0; k < KMAX; ++k) {
                     if (k >= K) break;
                     if (ranks[k] != rk[b] || rows[k] < 0) continue;
-                    char* out = (char*)a.packed + (int64_t)rows[k] * row_bytes;
+                    const RowOut out((char*)a.packed + (int64_t)rows[k] * row_bytes, row_bytes);
 #pragma unroll
                     for (int i = 0; i < VPT; ++i) {
                         const int v = base + tid + i * nth;
-                        if (v < nvec) st16_stream(out + (int64_t)v * 16, val[b][i]);
+                        if (v < nvec) out.st16(v * 16, val[b][i]);
                     }
                 }
             }
