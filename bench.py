@@ -219,18 +219,24 @@ def measure(moe, W, name, args, dev, graphs=True, y_fp8=False, fp4=False):
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
 
-    def step(i, events=None):
-        st = sets[i % len(sets)]
-        if events is not None:
-            events[0].record(stream)
+    def dispatch_call(st):
         moe.dispatch(st["x"], idx, E, fp8=fp8 and not fp4, out=st["o"], ws=ws, fp4=fp4)
-        if events is not None and len(events) == 3:
-            events[1].record(stream)
+
+    def combine_call(st):
         if y_fp8:
             qc = moe.combine_fp4 if fp4 else moe.combine_fp8
             qc(st["o"].packed, st["o"].scales, st["o"].tok_map, w, out=st["out"], out_weights=st["ow"])
         else:
             moe.combine(st["y"], st["o"].tok_map, w, out=st["out"], out_weights=st["ow"])
+
+    def step(i, events=None):
+        st = sets[i % len(sets)]
+        if events is not None:
+            events[0].record(stream)
+        dispatch_call(st)
+        if events is not None and len(events) == 3:
+            events[1].record(stream)
+        combine_call(st)
         if events is not None:
             events[-1].record(stream)
 
@@ -289,6 +295,33 @@ def measure(moe, W, name, args, dev, graphs=True, y_fp8=False, fp4=False):
         for st_, ref in zip(sets, eager_out):
             assert torch.equal(st_["out"].view(torch.int16), ref.view(torch.int16)), \
                 "graph replay output differs from the eager output"
+        # breakdown in graph mode: dispatch and combine captured as graphs of their own
+        gd, gc = [], []
+        with torch.cuda.stream(cs):
+            for st_ in sets:
+                for fn, lst in ((dispatch_call, gd), (combine_call, gc)):
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g, stream=cs):
+                        fn(st_)
+                    lst.append(g)
+        torch.cuda.synchronize()
+        for i in range(args.warmup):
+            gd[i % len(gd)].replay()
+            gc[i % len(gc)].replay()
+        evh = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_ev)]
+        for i in range(args.steps):
+            evh[i][0].record(stream)
+            gd[i % len(gd)].replay()
+            evh[i][1].record(stream)
+            gc[i % len(gc)].replay()
+            evh[i][2].record(stream)
+        torch.cuda.synchronize()
+        graph_disp_us = [evh[i][0].elapsed_time(evh[i][1]) * 1e3 for i in range(n_ev)]
+        graph_comb_us = [evh[i][1].elapsed_time(evh[i][2]) * 1e3 for i in range(n_ev)]
+        for st_, ref in zip(sets, eager_out):
+            assert torch.equal(st_["out"].view(torch.int16), ref.view(torch.int16)), \
+                "split graph replay output differs from the eager output"
+        del gs, gd, gc
         log(f"[bench] {name}: graph replays done, outputs equal to eager")
 
     # drop the first timed round (start transient)
@@ -300,9 +333,18 @@ def measure(moe, W, name, args, dev, graphs=True, y_fp8=False, fp4=False):
              dispatch_us=statistics.median(tail(disp_us)), combine_us=statistics.median(tail(comb_us)),
              combine_us_mean=statistics.mean(tail(comb_us)), wall_ms=wall_ms,
              disp_b=disp_b, comb_b=comb_b)
+    def spread(v):
+        v = tail(v)
+        return {"median": round(statistics.median(v), 2), "min": round(min(v), 2),
+                "std": round(statistics.pstdev(v), 2)}
+
+    r["timing"] = {"eager": {"pair": spread(pair_us), "dispatch": spread(disp_us),
+                             "combine": spread(comb_us)}}
     if graph_us is not None:
         r.update(graph_pair_us=statistics.median(tail(graph_us)), graph_pair_us_min=min(tail(graph_us)),
                  graph_pair_us_std=statistics.pstdev(tail(graph_us)))
+        r["timing"]["graph"] = {"pair": spread(graph_us), "dispatch": spread(graph_disp_us),
+                                "combine": spread(graph_comb_us)}
     del sets
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
@@ -544,7 +586,7 @@ def main():
                "routing": s2["routing"], "payload": "fp8_e4m3+f32_scale_per_128" if s2["fp8"] else "bf16",
                "pair_us": round(s2["pair_us"], 2), "pair_us_min": round(s2["pair_us_min"], 2),
                "pair_us_std": round(s2["pair_us_std"], 2), "dispatch_us": round(s2["dispatch_us"], 2),
-               "combine_us": round(s2["combine_us"], 2),
+               "combine_us": round(s2["combine_us"], 2), "timing_us": s2["timing"],
                "algorithmic_bytes": {"dispatch": s2["disp_b"], "combine": s2["comb_b"]},
                "achieved_gbps": round(g2, 1), "pct_hbm_peak": round(100 * g2 / HBM_PEAK_GBS, 2)}
         if "graph_pair_us" in s2:
@@ -626,6 +668,7 @@ def main():
         "dispatch_us": round(d_us, 2),
         "combine_us": round(c_us, 2),
         "dispatch_gbps": round(disp_gbs, 1),
+        "timing_us": r["timing"],
         "algorithmic_bytes": {"dispatch": disp_b, "combine": comb_b},
         "roofline": {"bound": "hbm", "kernel": "combine_kernel", "achieved": round(roof_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(roof_gbs / HBM_PEAK_GBS, 4),
