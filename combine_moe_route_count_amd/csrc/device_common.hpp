@@ -156,22 +156,28 @@ __device__ __forceinline__ void st8_stream(void* p, u32x2 v) {
 // A destination row addressed through a buffer resource.  The row base is
 // wave-uniform (a broadcast row index), so it stays in scalar registers and
 // each lane adds only its byte offset; an offset outside the row is dropped by
-// the hardware range check.  Stores carry the agent-scope streaming policy
-// (sc1 nt): written through L2 as data that is not read again soon.  On the
-// write-heavy dispatch this measured about 3% faster than the plain
-// non-temporal store (which keeps the line in L2 until eviction); on the
-// read-heavy combine the two were equal.
+// the hardware range check.  POL is the stores' cache policy, chosen per row
+// kind by measurement on 1 GiB-class scatters:
+//   kStoreThrough (sc1 nt, agent-scope streaming: written through L2) for the
+//     fp8 / fp4 rows (7 KB and less at H=7168), where it beat the plain
+//     non-temporal store by about 3% and plain stores lost 10%, and for the
+//     dedup expansion, whose source rows are read back from HBM as it goes;
+//   kStorePlain (write-back through L2) for the copies of token rows in bf16
+//     or f32 (14-16 KB), 3% (bf16 dispatch) to 4% (f32 dedup recv copy) faster;
+// the pure-write ceilings are 5.45 TB/s plain, 5.0 sc1 nt, 4.9 nt.
 constexpr int kStoreThrough = (1 << 4) | (1 << 1);  // cache policy bits: sc1, nt
+constexpr int kStorePlain = 0;
 constexpr int kRsrcWord3 = 0x00020000;               // gfx9 descriptor word 3: 32-bit raw data
+template <int POL>
 struct RowOut {
     __amdgpu_buffer_rsrc_t r;
     __device__ __forceinline__ RowOut(void* row, int64_t bytes)
         : r(__builtin_amdgcn_make_buffer_rsrc(row, 0, (int)bytes, kRsrcWord3)) {}
     __device__ __forceinline__ void st16(int off, u32x4 v) const {
-        __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kStoreThrough);
+        __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, POL);
     }
     __device__ __forceinline__ void st8(int off, u32x2 v) const {
-        __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kStoreThrough);
+        __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, POL);
     }
 };
 

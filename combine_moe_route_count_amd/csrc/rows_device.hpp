@@ -39,8 +39,9 @@ __device__ __forceinline__ void settle(u32x4 (&v)[N]) {
 }
 
 // Copy one row of nvec 16-byte vectors (already holding pass 0 in val) to up
-// to D destination rows; passes after the first reload from src.
-template <int DMAX, int VPT>
+// to D destination rows with store policy POL; passes after the first reload
+// from src.
+template <int DMAX, int VPT, int POL>
 __device__ __forceinline__ void store_row_copies(const char* src, int nvec, char* dst,
                                                  int64_t row_bytes, const int (&rows)[DMAX], int D,
                                                  u32x4 (&val)[VPT], int tid, int nthreads) {
@@ -55,7 +56,7 @@ __device__ __forceinline__ void store_row_copies(const char* src, int nvec, char
         for (int d = 0; d < DMAX; ++d) {
             if (d >= D) break;
             if (rows[d] < 0) continue;
-            const RowOut out(dst + (int64_t)rows[d] * row_bytes, row_bytes);
+            const RowOut<POL> out(dst + (int64_t)rows[d] * row_bytes, row_bytes);
 #pragma unroll
             for (int i = 0; i < VPT; ++i) {
                 const int v = base + tid + i * nthreads;

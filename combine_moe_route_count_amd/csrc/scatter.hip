@@ -83,7 +83,10 @@ __device__ __forceinline__ void scatter_copy_kernel_item(const ScatterArgs& a, i
     // scales first: loading them after the row stores would reuse registers the
     // stores still read, and the compiler would wait for every store first
     if (SC) forward_scales<DMAX>(a, t, rows, nth);
-    store_row_copies<DMAX, VPT>(src, nvec, (char*)a.packed, row_bytes, rows, a.slot.K, val, tid, nth);
+    // SC: pre-quantized fp8 rows; otherwise bf16 / f32 row copies
+    store_row_copies<DMAX, VPT, SC ? kStoreThrough : kStorePlain>(src, nvec, (char*)a.packed,
+                                                                   row_bytes, rows, a.slot.K, val,
+                                                                   tid, nth);
 }
 
 // ---------------------------------------------------------------------------
@@ -129,7 +132,7 @@ __device__ __forceinline__ void scatter_fp8_kernel_item(const ScatterArgs& a, in
         for (int d = 0; d < DMAX; ++d) {
             if (d >= K) break;
             if (rows[d] < 0) continue;
-            const RowOut out((char*)a.packed + (int64_t)rows[d] * prow, prow);
+            const RowOut<kStoreThrough> out((char*)a.packed + (int64_t)rows[d] * prow, prow);
             float* sc = a.scales + (int64_t)rows[d] * nblk;
 #pragma unroll
             for (int i = 0; i < UPT; ++i) {
@@ -186,7 +189,8 @@ __device__ __forceinline__ void recv_copy_kernel_item(const RecvArgs& a, int64_t
     }
     int rows[DMAX];
     broadcast_rows<DMAX>(my_row, rows);
-    store_row_copies<DMAX, VPT>(src, nvec, (char*)a.recv_x, row_bytes, rows, R, val, tid, nth);
+    store_row_copies<DMAX, VPT, kStorePlain>(src, nvec, (char*)a.recv_x, row_bytes, rows, R, val,
+                                             tid, nth);
 }
 
 // ---------------------------------------------------------------------------
@@ -259,7 +263,8 @@ __device__ __forceinline__ void expand_kernel_item(const ExpandArgs& a, int64_t 
                 for (int k = 0; k < KMAX; ++k) {
                     if (k >= K) break;
                     if (ranks[k] != rk[b] || rows[k] < 0) continue;
-                    const RowOut out((char*)a.packed + (int64_t)rows[k] * row_bytes, row_bytes);
+                    const RowOut<kStoreThrough> out((char*)a.packed + (int64_t)rows[k] * row_bytes,
+                                                    row_bytes);
 #pragma unroll
                     for (int i = 0; i < VPT; ++i) {
                         const int v = base + tid + i * nth;
