@@ -149,9 +149,6 @@ __device__ __forceinline__ void st16_stream(void* p, u32x4 v) {
 __device__ __forceinline__ u32x2 ld8_stream(const void* p) {
     return __builtin_nontemporal_load((const u32x2*)p);
 }
-__device__ __forceinline__ void st8_stream(void* p, u32x2 v) {
-    __builtin_nontemporal_store(v, (u32x2*)p);
-}
 
 // A destination row addressed through a buffer resource.  The row base is
 // wave-uniform (a broadcast row index), so it stays in scalar registers and
