@@ -131,6 +131,104 @@ def pmc_summary(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, out_json):
     print(json.dumps(d, indent=1))
 
 
+PROFILE_RUNS = {
+    "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d {d}/trace -o bench -- "
+             "python bench.py --steps 10 --warmup 5 --no-cpu --secondary none",
+    "FETCH_SIZE": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/FETCH_SIZE -o bench -- "
+                  "python bench.py --steps 5 --warmup 2 --no-cpu --no-graph --secondary none "
+                  "--no-fp8-combine --no-dedup",
+    "WRITE_SIZE": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/WRITE_SIZE -o bench -- "
+                  "python bench.py --steps 5 --warmup 2 --no-cpu --no-graph --secondary none "
+                  "--no-fp8-combine --no-dedup",
+    "cal_FETCH_SIZE": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/cal_FETCH_SIZE -o copy -- "
+                      "python bench.py --calibrate-copy --steps 3",
+    "cal_WRITE_SIZE": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/cal_WRITE_SIZE -o copy -- "
+                      "python bench.py --calibrate-copy --steps 3",
+}
+
+
+def _short_kernel(name):
+    import re
+    name = re.sub(r"^void ", "", name)
+    name = name.replace("moe::(anonymous namespace)::", "").replace("moe::", "")
+    if not name.startswith("at::"):
+        name = re.sub(r"\(.*$", "", name)
+    return name[:90]
+
+
+def profile_text(prof_dir, out_dir):
+    """Text summaries of the rocprofv3 runs in PROFILE_RUNS (run with -d prof_dir):
+    per-kernel trace statistics, HBM bytes per dispatch from FETCH_SIZE / WRITE_SIZE
+    scaled by the 1 GiB calibration copy, and the combine's counter JSON."""
+    import collections
+    import csv
+    cmd = {k: v.format(d=prof_dir) for k, v in PROFILE_RUNS.items()}
+    work = "skewed_fp8 workload (T=8192 H=7168 E=256 K=8, Zipf 1.2, fp8 payload), MI355X"
+    stats = list(csv.DictReader(open(os.path.join(prof_dir, "trace", "bench_kernel_stats.csv"))))
+    avg_us = {}
+    out = [f"# Kernel trace: {work}", f"# command: {cmd['trace']}",
+           "# (bench.py: the headline pair (3 setup dispatches + dequants, 5 warmup, 2x10 timed,",
+           "#  3 + 5 + 10 graph-replayed pairs and as many split dispatch / combine replays), the",
+           "#  fp8-input combine pair, the fp4 payload pair, the dispatch variants (replay,",
+           "#  pre-quantized), the dedup workload line (T=16384 H=4096 E=64 K=6 R=8 f32) and the",
+           "#  1 GiB 16-byte copy ceiling: 3 warmup + 10 timed copies)",
+           f"# summary: python bench.py --profile-text {prof_dir} profiles",
+           "# kernel | calls | avg us | min us | max us | % of GPU time", ""]
+    for r in stats:
+        k = _short_kernel(r["Name"])
+        avg_us.setdefault(k, float(r["AverageNs"]) / 1e3)
+        out.append(f"{k:70s} {int(r['Calls']):5d} {float(r['AverageNs']) / 1e3:9.2f} "
+                   f"{float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f} "
+                   f"{float(r['Percentage']):6.2f}")
+    with open(os.path.join(out_dir, "skewed_fp8_kernel_trace.txt"), "w") as fh:
+        fh.write("\n".join(out) + "\n")
+
+    def per_kernel(sub, name):
+        d = collections.defaultdict(list)
+        for r in csv.DictReader(open(os.path.join(prof_dir, sub, name))):
+            d[_short_kernel(r["Kernel_Name"])].append(float(r["Counter_Value"]))
+        return d
+
+    fetch = per_kernel("FETCH_SIZE", "bench_counter_collection.csv")
+    write = per_kernel("WRITE_SIZE", "bench_counter_collection.csv")
+    cf = statistics.mean(x for x in per_kernel("cal_FETCH_SIZE", "copy_counter_collection.csv")
+                         ["copy16_kernel"] if x > 0)
+    cw = statistics.mean(x for x in per_kernel("cal_WRITE_SIZE", "copy_counter_collection.csv")
+                         ["copy16_kernel"] if x > 0)
+    fs, wsc = COPY_BYTES / cf, COPY_BYTES / cw
+    lines = [f"# HBM traffic per dispatch from rocprofv3 counters: {work}", "# commands:"]
+    lines += [f"#   {cmd[k]}" for k in ("FETCH_SIZE", "WRITE_SIZE", "cal_FETCH_SIZE", "cal_WRITE_SIZE")]
+    lines += [f"#   python bench.py --profile-text {prof_dir} profiles",
+              f"# calibration: the library's 16-byte copy of 1 GiB reads FETCH_SIZE {cf:.0f} and "
+              f"WRITE_SIZE {cw:.0f};",
+              f"#   bytes per counter unit: fetch {fs:.1f}, write {wsc:.1f}",
+              "# kernel | dispatches | fetch MB | write MB (averages per dispatch, scaled) | "
+              "GB/s over the trace's average duration", ""]
+    tot = {}
+    for k in fetch:
+        if k not in write:
+            continue
+        fb = statistics.mean(fetch[k]) * fs
+        wb = statistics.mean(write[k]) * wsc
+        tot[k] = fb + wb
+        rate = f"{(fb + wb) / (avg_us[k] * 1e3):10.1f}" if k in avg_us else f"{'':>10s}"
+        lines.append(f"{k:70s} {len(fetch[k]):4d} {fb / 1e6:10.2f} {wb / 1e6:10.2f} {rate}")
+    comb, scat, route = ("combine_kernel<false, false, 8>", "scatter_fp8_kernel<8, 2, false, false>",
+                         "route_fused_kernel<ExpertKeys>")
+    disp_b, comb_b = algorithmic_bytes(8192, 7168, 8, 256, 8192 * 8, fp8=True)
+    lines += ["", f"combine_kernel algorithmic bytes per launch: {comb_b}; counters: "
+                  f"{tot[comb]:.0f} ({tot[comb] / comb_b:.4f}x)",
+              f"dispatch (route_fused + scatter_fp8) algorithmic bytes per call: {disp_b}; "
+              f"counters: {tot[route] + tot[scat]:.0f} ({(tot[route] + tot[scat]) / disp_b:.4f}x)"]
+    with open(os.path.join(out_dir, "skewed_fp8_hbm_counters.txt"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    pmc_summary(os.path.join(prof_dir, "FETCH_SIZE", "bench_counter_collection.csv"),
+                os.path.join(prof_dir, "WRITE_SIZE", "bench_counter_collection.csv"),
+                os.path.join(prof_dir, "cal_FETCH_SIZE", "copy_counter_collection.csv"),
+                os.path.join(prof_dir, "cal_WRITE_SIZE", "copy_counter_collection.csv"),
+                os.path.join(out_dir, "combine_skewed_fp8_pmc.json"))
+
+
 def _cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -537,12 +635,17 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=1024)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run the plain 1 GiB copy used to scale HBM counters")
+    ap.add_argument("--profile-text", nargs=2, metavar=("PROF_DIR", "OUT_DIR"),
+                    help="write the text summaries of the rocprofv3 runs listed in PROFILE_RUNS")
     ap.add_argument("--pmc-summary", nargs=5, metavar=("FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE", "OUT"),
                     help="summarize rocprofv3 FETCH_SIZE / WRITE_SIZE csvs into OUT (json)")
     args = ap.parse_args()
 
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary)
+        return
+    if args.profile_text:
+        profile_text(*args.profile_text)
         return
 
     if args.gpus != 1:
