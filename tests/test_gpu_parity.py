@@ -811,3 +811,134 @@ def test_quantized_combine_and_replay_empty(fmt):
     torch.cuda.synchronize()
     assert out.shape == (0, H) and ow.shape == (0,)
 
+
+
+# ---------------------------------------------------------------------------
+# guard rows: buffers longer than the row counts passed in; nothing past them
+# is written (the row stores go through per-row buffer descriptors, so this
+# checks the row indices they are given)
+# ---------------------------------------------------------------------------
+
+_GUARD = 5
+
+
+def _guard_intact(t, rows, name):
+    tail = host(t[rows:]).view(np.uint8)
+    poison = oracle.POISON_BYTE if t.dtype != torch.int32 else None
+    if poison is None:
+        assert (host(t[rows:]) == oracle.POISON_I32).all(), f"{name}: guard rows written"
+    else:
+        assert (tail == poison).all(), f"{name}: guard rows written"
+
+
+@pytest.mark.parametrize("payload", ["bf16", "f32", "fp8", "fp4", "prequant"])
+@pytest.mark.parametrize("layout", ["compact_short", "padded_tight"])
+def test_dispatch_guard_rows(payload, layout):
+    T, H, K, E = 700, 256, 6, 16
+    rng = np.random.default_rng(91)
+    idx = _mixed_idx(rng, T, K, E)
+    flat = idx.ravel()
+    cnt = np.bincount(flat[(flat >= 0) & (flat < E)], minlength=E)
+    cap = 0 if layout == "compact_short" else max(1, int(cnt.max()) // 2)
+    rows = int(cnt.sum()) - 41 if cap == 0 else E * cap - 3
+    quant = payload in ("fp8", "fp4", "prequant")
+    x_dt = {"f32": torch.float32}.get(payload, torch.bfloat16)
+    note(f"dispatch guard rows {payload} {layout} rows={rows}")
+    o = moe._lib.alloc_dispatch(T, H, K, E, rows + _GUARD, torch.uint8 if quant else x_dt, quant,
+                                DEV, fp4=payload == "fp4")
+    for t in (o.packed, o.scales, o.packed_src, o.tok_map, o.packed_cnt, o.packed_off, o.stats):
+        poison_(t)
+    if payload == "prequant":
+        q = rng.integers(0, 256, size=(T, H), dtype=np.uint8)
+        sc = (rng.random((T, H // 128)) + 0.5).astype(np.float32)
+        moe.dispatch_prequant(dev(q), dev(sc), dev(idx), E, cap=cap, packed_rows=rows, out=o)
+        ref = oracle.dispatch(q, "fp8", idx, E, cap=cap, packed_rows=rows, x_scales=sc)
+    else:
+        dt = "f32" if payload == "f32" else "bf16"
+        x = W.normal_x(rng, T, H, dt)
+        moe.dispatch(dev_x(x, dt), dev(idx), E, cap=cap, packed_rows=rows, fp8=payload == "fp8",
+                     fp4=payload == "fp4", out=o)
+        ref = oracle.dispatch(x, dt, idx, E, cap=cap, packed_rows=rows,
+                              packed_dt=payload if quant else None)
+    torch.cuda.synchronize()
+    view = moe._lib.DispatchOut(packed=o.packed[:rows],
+                                scales=o.scales[:rows] if quant else None,
+                                packed_cnt=o.packed_cnt, packed_off=o.packed_off,
+                                packed_src=o.packed_src[:rows], tok_map=o.tok_map, stats=o.stats)
+    assert_dispatch_equal(view, ref, fp8=quant)
+    _guard_intact(o.packed, rows, "packed")
+    _guard_intact(o.packed_src, rows, "packed_src")
+    if quant:
+        _guard_intact(o.scales, rows, "scales")
+
+
+@pytest.mark.parametrize("payload", ["bf16", "fp8", "fp4", "prequant"])
+def test_replay_guard_rows(payload):
+    """Replay into the first `rows` rows of a longer buffer, with cached rows at
+    and past the limit: those entries are skipped and the guard stays."""
+    T, H, K = 400, 256, 4
+    rows = T * K - 50
+    rng = np.random.default_rng(92)
+    tm = rng.permutation(T * K + 2 * _GUARD)[:T * K].astype(np.int64).reshape(T, K)
+    tm[rng.random((T, K)) < 0.05] = -1
+    tm[0, 0], tm[1, 1] = rows, rows + _GUARD + 7          # just past the limit, past the guard
+    quant = payload != "bf16"
+    width = H // 2 if payload == "fp4" else H
+    packed = torch.empty((rows + _GUARD, width), dtype=torch.uint8 if quant else torch.bfloat16,
+                         device=DEV)
+    scales = torch.empty((rows + _GUARD, H // 128), dtype=torch.float32, device=DEV) if quant else None
+    poison_(packed)
+    if quant:
+        poison_(scales)
+    note(f"replay guard rows {payload} rows={rows}")
+    if payload == "prequant":
+        q = rng.integers(0, 256, size=(T, H), dtype=np.uint8)
+        sc = (rng.random((T, H // 128)) + 0.5).astype(np.float32)
+        moe.dispatch_replay(dev(q), dev(tm), packed[:rows], scales=scales[:rows], x_scales=dev(sc))
+        ref = oracle.dispatch_replay(q, "fp8", tm, rows, x_scales=sc)
+    else:
+        x = W.normal_x(rng, T, H, "bf16")
+        moe.dispatch_replay(dev_bf16(x), dev(tm), packed[:rows],
+                            scales=scales[:rows] if quant else None, fp4=payload == "fp4")
+        ref = oracle.dispatch_replay(x, "bf16", tm, rows, packed_dt=payload if quant else None)
+    torch.cuda.synchronize()
+    got = host(packed[:rows]).view(np.uint8)
+    np.testing.assert_array_equal(got, ref["packed"].view(np.uint8).reshape(got.shape))
+    if quant:
+        np.testing.assert_array_equal(host(scales[:rows]).view(np.uint32),
+                                      ref["scales"].view(np.uint32))
+    _guard_intact(packed, rows, "packed")
+    if quant:
+        _guard_intact(scales, rows, "scales")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_dedup_guard_rows(dtype):
+    T, H, K, E, R = 600, 128, 6, 32, 8
+    rng = np.random.default_rng(93)
+    idx = _mixed_idx(rng, T, K, E)
+    x = W.normal_x(rng, T, H, dtype)
+    full = oracle.dedup_dispatch(x, dtype, idx, E, R)
+    recv_rows = int(full["recv_cnt"].sum()) - 23
+    packed_rows = int(full["packed_cnt"].sum()) - 31
+    note(f"dedup guard rows {dtype} recv_rows={recv_rows} packed_rows={packed_rows}")
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    o = moe._lib.alloc_dedup(T, H, K, E, R, recv_rows + _GUARD, packed_rows + _GUARD, tdt, DEV)
+    for f in ("recv_x", "recv_cnt", "recv_off", "recv_src", "rank_slot", "packed", "packed_cnt",
+              "packed_off", "packed_src", "tok_map", "stats"):
+        poison_(getattr(o, f))
+    moe.dedup_dispatch(dev_x(x, dtype), dev(idx), E, R, recv_rows=recv_rows,
+                       packed_rows=packed_rows, out=o)
+    torch.cuda.synchronize()
+    ref = oracle.dedup_dispatch(x, dtype, idx, E, R, recv_rows=recv_rows, packed_rows=packed_rows)
+    for f in ("recv_cnt", "recv_off", "rank_slot", "packed_cnt", "packed_off", "tok_map", "stats"):
+        np.testing.assert_array_equal(host(getattr(o, f)), ref[f], err_msg=f)
+    np.testing.assert_array_equal(host(o.recv_src[:recv_rows]), ref["recv_src"])
+    np.testing.assert_array_equal(host(o.packed_src[:packed_rows]), ref["packed_src"])
+    np.testing.assert_array_equal(host(o.recv_x[:recv_rows]).view(np.uint8),
+                                  ref["recv_x"].view(np.uint8))
+    np.testing.assert_array_equal(host(o.packed[:packed_rows]).view(np.uint8),
+                                  ref["packed"].view(np.uint8))
+    for f, n in (("recv_x", recv_rows), ("recv_src", recv_rows), ("packed", packed_rows),
+                 ("packed_src", packed_rows)):
+        _guard_intact(getattr(o, f), n, f)
