@@ -942,3 +942,57 @@ def test_dedup_guard_rows(dtype):
     for f, n in (("recv_x", recv_rows), ("recv_src", recv_rows), ("packed", packed_rows),
                  ("packed_src", packed_rows)):
         _guard_intact(getattr(o, f), n, f)
+
+
+# ---------------------------------------------------------------------------
+# soak: a random T in [0, Tmax] per call on reused buffers and one workspace
+# ---------------------------------------------------------------------------
+
+def test_soak_random_T():
+    """1000 rounds of dispatch + combine, bf16 and fp8 payloads alternating, T
+    drawn from [0, Tmax] each time (T = 0 included), every round against the
+    oracle; the buffers and the workspace are allocated once for Tmax."""
+    Tmax, H, K, E = 600, 256, 4, 24
+    rng = np.random.default_rng(77)
+    ws = moe.workspace(Tmax, K, E, 0, DEV)
+    ob = moe._lib.alloc_dispatch(Tmax, H, K, E, Tmax * K, torch.bfloat16, False, DEV)
+    oq = moe._lib.alloc_dispatch(Tmax, H, K, E, Tmax * K, torch.uint8, True, DEV)
+    out = torch.empty((Tmax, H), dtype=torch.bfloat16, device=DEV)
+    ow = torch.empty(Tmax, dtype=torch.float32, device=DEV)
+    for r in range(1000):
+        T = 0 if r % 50 == 7 else int(rng.integers(1, Tmax + 1))
+        fp8 = r % 2 == 1
+        idx = rng.integers(-1, E, size=(T, K)).astype(np.int32)
+        x = W.normal_x(rng, T, H, "bf16")
+        w = rng.random((T, K)).astype(np.float32)
+        o = oq if fp8 else ob
+        rows = T * K
+        xd = dev_bf16(x) if T else torch.empty((0, H), dtype=torch.bfloat16, device=DEV)
+        idd = dev(idx) if T else torch.empty((0, K), dtype=torch.int32, device=DEV)
+        wd = dev(w) if T else torch.empty((0, K), dtype=torch.float32, device=DEV)
+        moe.dispatch(xd, idd, E, packed_rows=rows, fp8=fp8, out=o, ws=ws)
+        tm = o.tok_map[:T]
+        if fp8:
+            moe.combine_fp8(o.packed[:rows], o.scales[:rows], tm, wd, out=out[:T], out_weights=ow[:T])
+        else:
+            moe.combine(o.packed[:rows], tm, wd, out=out[:T], out_weights=ow[:T])
+        torch.cuda.synchronize()
+        ref = oracle.dispatch(x, "bf16", idx, E, packed_rows=rows, packed_dt="fp8" if fp8 else None)
+        view = moe._lib.DispatchOut(packed=o.packed[:rows], scales=o.scales[:rows] if fp8 else None,
+                                    packed_cnt=o.packed_cnt, packed_off=o.packed_off,
+                                    packed_src=o.packed_src[:rows], tok_map=tm, stats=o.stats)
+        np.testing.assert_array_equal(host(tm), ref["tok_map"], err_msg=f"round {r} T={T}")
+        np.testing.assert_array_equal(host(o.packed_cnt), ref["packed_cnt"])
+        np.testing.assert_array_equal(host(o.stats), ref["stats"])
+        if T == 0:
+            continue
+        valid = ref["tok_map"] >= 0
+        used = np.unique(ref["tok_map"][valid])
+        got = host(view.packed).view(np.uint8)[used]
+        np.testing.assert_array_equal(got, ref["packed"].view(np.uint8)[used], err_msg=f"round {r}")
+        if fp8:
+            eo, ew = oracle.combine_fp8(ref["packed"], ref["scales"], ref["tok_map"], w, "bf16")
+        else:
+            eo, ew = oracle.combine(ref["packed"], "bf16", ref["tok_map"], w, "bf16")
+        _check_combine(host(out[:T]), eo, "bf16")
+        np.testing.assert_array_equal(host(ow[:T]).view(np.uint32), ew.view(np.uint32))
