@@ -176,17 +176,23 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(CombineArgs a, in
 
 // ---------------------------------------------------------------------------
 // combine of fp8 expert outputs: v = f32(q) * s (the row's block scale, 1 for
-// the direct cast), then acc = acc + w_k * v for k ascending.  A lane-unit is
-// 16 elements: one 16-byte load of codes per row (the same bytes in flight as
-// the bf16 form's 8 elements) plus the row's scale, dequantized two codes per
-// v_cvt_pk_f32_fp8 inside the reduce.  FP4: e2m1 codes, two per byte, an
-// 8-byte load per row, eight codes per gfx950 scaled conversion (scale 1).
+// the direct cast), then acc = acc + w_k * v for k ascending.  Each lane loads
+// 8 bytes of codes per row plus the row's scale and dequantizes inside the
+// reduce: e4m3, 8 elements per lane-unit, two codes per v_cvt_pk_f32_fp8; FP4,
+// e2m1, 16 elements per lane-unit, eight codes per gfx950 scaled conversion
+// (scale 1).  Both forms stay under 64 VGPRs (8 waves per SIMD): the e4m3 one
+// ran 104 us against 106.6 with 16-element units (88 VGPRs), the e2m1 one 71.1
+// against 73.1 with its codes held in the wider array (76 VGPRs); 8-element
+// e2m1 units (4-byte loads) took 84 us.
 // ---------------------------------------------------------------------------
+constexpr int quant_unit_elems(bool fp4) { return fp4 ? 16 : 8; }
 template <bool OF32, int KMAX, bool FP4>
 __device__ __forceinline__ void combine_fp8_item(const CombineArgs& a, int64_t t, int c, int C) {
+    constexpr int EL = quant_unit_elems(FP4);
     const int64_t H = a.H;
-    const int units = (int)(H / 16);
+    const int units = (int)(H / EL);
     const int64_t nblk = H / kFp8Block;
+    const int64_t row_bytes = FP4 ? H / 2 : H;
     int rows[KMAX];
     float w[KMAX];
     token_entries<KMAX>(a, t, rows, w);
@@ -194,27 +200,25 @@ __device__ __forceinline__ void combine_fp8_item(const CombineArgs& a, int64_t t
     const int u = c * C + (int)threadIdx.x;
     if ((int)threadIdx.x < C && u < units) {
         const uint8_t* q = (const uint8_t*)a.y;
-        u32x4 code[KMAX];
-        u32x2 code4[KMAX];
+        u32x2 code[KMAX];
         float scl[KMAX];
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) {
             if (rows[k] < 0) continue;
-            if (FP4) code4[k] = ld8_stream(q + (int64_t)rows[k] * (H / 2) + (int64_t)u * 8);
-            else code[k] = ld16_stream(q + (int64_t)rows[k] * H + (int64_t)u * 16);
-            scl[k] = a.y_scales ? a.y_scales[(int64_t)rows[k] * nblk + u / (kFp8Block / 16)] : 1.0f;
+            code[k] = ld8_stream(q + (int64_t)rows[k] * row_bytes + (int64_t)u * 8);
+            scl[k] = a.y_scales ? a.y_scales[(int64_t)rows[k] * nblk + u / (kFp8Block / EL)] : 1.0f;
         }
-        float acc[16];
+        float acc[EL];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) acc[j] = 0.0f;
+        for (int j = 0; j < EL; ++j) acc[j] = 0.0f;
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) {
             if (rows[k] < 0) continue;
-            float v[16];
-            if (FP4) {
+            float v[EL];
+            if constexpr (FP4) {
                 float h0[8], h1[8];
-                unpack_e2m1x8(code4[k][0], h0);
-                unpack_e2m1x8(code4[k][1], h1);
+                unpack_e2m1x8(code[k][0], h0);
+                unpack_e2m1x8(code[k][1], h1);
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     v[j] = h0[j];
@@ -222,7 +226,7 @@ __device__ __forceinline__ void combine_fp8_item(const CombineArgs& a, int64_t t
                 }
             } else {
 #pragma unroll
-                for (int d = 0; d < 4; ++d) {
+                for (int d = 0; d < 2; ++d) {
                     unpack_e4m3x2<false>(code[k][d], v[4 * d], v[4 * d + 1]);
                     unpack_e4m3x2<true>(code[k][d], v[4 * d + 2], v[4 * d + 3]);
                 }
@@ -232,27 +236,26 @@ __device__ __forceinline__ void combine_fp8_item(const CombineArgs& a, int64_t t
             // VALU, not HBM, is what the quantized forms run short of
             if (ballot64(scl[k] != 1.0f) == 0) {
 #pragma unroll
-                for (int j = 0; j < 16; ++j) {
+                for (int j = 0; j < EL; ++j) {
                     const float p = w[k] * v[j];
                     acc[j] = acc[j] + p;
                 }
             } else {
 #pragma unroll
-                for (int j = 0; j < 16; ++j) {
+                for (int j = 0; j < EL; ++j) {
                     const float dq = v[j] * scl[k];
                     const float p = w[k] * dq;
                     acc[j] = acc[j] + p;
                 }
             }
         }
-        float lo[8], hi[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            lo[j] = acc[j];
-            hi[j] = acc[8 + j];
+        for (int h = 0; h < EL / 8; ++h) {
+            float part[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) part[j] = acc[8 * h + j];
+            store_unit<OF32>(a.out, t, H, (int64_t)u * EL + 8 * h, part);
         }
-        store_unit<OF32>(a.out, t, H, (int64_t)u * 16, lo);
-        store_unit<OF32>(a.out, t, H, (int64_t)u * 16 + 8, hi);
     }
     if (c == 0 && threadIdx.x == 0 && a.out_weights) {
         float s = 0.0f;
@@ -489,7 +492,7 @@ void by_k(const CombineArgs& a, hipStream_t s) {
 
 template <bool OF32, int KMAX, bool FP4>
 void fp8_go(const CombineArgs& a, hipStream_t s) {
-    const Chunking ch = chunking(a.H, 16);
+    const Chunking ch = chunking(a.H, quant_unit_elems(FP4));
     combine_fp8_kernel<OF32, KMAX, FP4>
         <<<item_grid(a.T * ch.nch), dim3(threads_for(ch.C)), 0, s>>>(a, ch.C, ch.nch);
 }
