@@ -1,14 +1,15 @@
 // combine.hip - weighted gather-reduce of each token's expert outputs back to
 // token order, plus out_weights.
 //
-// One workgroup per token.  Lanes below K read the token's tok_map entries and
-// weights once and broadcast them to the wave with readlane, so every branch
-// on an entry is wave-uniform.  Each lane owns units of 8 elements: it first
-// issues the 16-byte loads of all K rows for its units (the load-first gather
-// of "feat(EPv2): [preview] internode dispatch/combine over CCO/GDA", ROCm/mori
-// pull 625, commit log: 16 B vector gather), then reduces in f32 in ascending
-// k with a separately rounded multiply and add (the build disables
-// contraction), and stores 16 bytes of bf16 (or 32 bytes of f32).  The weight
+// One workgroup per (token, chunk of the row).  Lanes below K read the token's
+// tok_map entries and weights once and broadcast them to the wave with
+// readlane, so every branch on an entry is wave-uniform.  Each lane owns a unit
+// of 8 bf16 or 4 f32 elements: it first issues the 16-byte loads of all K rows
+// for its unit (the load-first gather of "feat(EPv2): [preview] internode
+// dispatch/combine over CCO/GDA", ROCm/mori pull 625, commit log: 16 B vector
+// gather), then reduces in f32 in ascending k with a separately rounded
+// multiply and add (the build disables contraction), and stores the unit as
+// bf16 or f32.  The weight
 // sum is folded in once per token ("Draft: cco + flydsl dispatch/combine",
 // ROCm/mori pull 448, commit log: out_weights folded into the gather loop).
 //
@@ -25,7 +26,13 @@ namespace {
 
 constexpr int kCombThreads = 256;
 
-// 8 consecutive elements of row `row` starting at element col, as f32.
+// Elements per lane-unit of the gathers: one 16-byte load per row, 8 bf16 or
+// 4 f32.  The 4-element f32 unit keeps the f32 forms under 64 VGPRs (8 waves
+// per SIMD) as the bf16 ones are.
+constexpr int unit_elems(bool yf32) { return yf32 ? 4 : 8; }
+
+// unit_elems(YF32) consecutive elements of row `row` starting at element col,
+// as f32.
 template <bool YF32>
 struct Unit;
 
@@ -43,41 +50,48 @@ struct Unit<false> {  // bf16: one 16-byte load
 };
 
 template <>
-struct Unit<true> {  // f32: two 16-byte loads
-    u32x4 a, b;
-    __device__ __forceinline__ void clear() {
-        a = u32x4{0, 0, 0, 0};
-        b = u32x4{0, 0, 0, 0};
-    }
-    __device__ __forceinline__ void settle() { asm volatile("" : "+v"(a), "+v"(b)); }
+struct Unit<true> {  // f32: one 16-byte load
+    u32x4 a;
+    __device__ __forceinline__ void clear() { a = u32x4{0, 0, 0, 0}; }
+    __device__ __forceinline__ void settle() { asm volatile("" : "+v"(a)); }
     __device__ __forceinline__ void load(const void* y, int64_t row, int64_t H, int64_t col) {
-        const float* p = (const float*)y + row * H + col;
-        a = ld16_stream(p);
-        b = ld16_stream(p + 4);
+        a = ld16_stream((const float*)y + row * H + col);
     }
     __device__ __forceinline__ float get(int j) const {
-        return __builtin_bit_cast(float, j < 4 ? a[j] : b[j - 4]);
+        // copied to a scalar first: this compiler's __builtin_bit_cast of a
+        // vector-element lvalue (a[j] directly) reads element 0 for every j
+        const uint32_t v = a[j];
+        return __builtin_bit_cast(float, v);
     }
 };
 
-template <bool OF32>
+// EL (4 or 8) results of one lane-unit, stored as f32 (16-byte stores) or
+// bf16 (one 16-byte store of 8, or one 8-byte store of 4).
+template <bool OF32, int EL>
 __device__ __forceinline__ void store_unit(void* out, int64_t row, int64_t H, int64_t col,
-                                           const float (&acc)[8]) {
-    if (OF32) {
+                                           const float (&acc)[EL]) {
+    static_assert(EL == 4 || EL == 8, "lane-unit of 4 or 8 elements");
+    // if constexpr: the branches index acc up to 7, which must not even be
+    // instantiated for a 4-element unit
+    if constexpr (OF32) {
         float* p = (float*)out + row * H + col;
-        u32x4 a, b;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            a[j] = __builtin_bit_cast(uint32_t, acc[j]);
-            b[j] = __builtin_bit_cast(uint32_t, acc[4 + j]);
+        for (int h = 0; h < EL / 4; ++h) {
+            u32x4 a;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) a[j] = __builtin_bit_cast(uint32_t, acc[4 * h + j]);
+            st16_stream(p + 4 * h, a);
         }
-        st16_stream(p, a);
-        st16_stream(p + 4, b);
-    } else {
+    } else if constexpr (EL == 8) {
         u32x4 a;
 #pragma unroll
         for (int j = 0; j < 4; ++j) a[j] = pack_bf16x2(acc[2 * j], acc[2 * j + 1]);
         st16_stream((uint16_t*)out + row * H + col, a);
+    } else {
+        u32x2 a;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) a[j] = pack_bf16x2(acc[2 * j], acc[2 * j + 1]);
+        __builtin_nontemporal_store(a, (u32x2*)((uint16_t*)out + row * H + col));
     }
 }
 
@@ -105,7 +119,7 @@ __device__ __forceinline__ void token_entries(const CombineArgs& a, int64_t t, i
 }
 
 // Work decomposition: workgroup (c, t) owns units [c*C, c*C + C) of token t,
-// one 8-element unit per lane, so every lane issues the loads of all K rows at
+// one lane-unit per lane, so every lane issues the loads of all K rows at
 // once and there is no second pass.  Chunks of at most kChunkUnits units keep
 // the workgroups small enough that several fit on a CU and one workgroup's
 // routing round trip overlaps with the others' gathers.
@@ -130,8 +144,9 @@ inline Chunking chunking(int64_t H, int unit_elems = 8) {
 // ---------------------------------------------------------------------------
 template <bool YF32, bool OF32, int KMAX>
 __device__ __forceinline__ void combine_item(const CombineArgs& a, int64_t t, int c, int C) {
+    constexpr int EL = unit_elems(YF32);
     const int64_t H = a.H;
-    const int units = (int)(H / 8);
+    const int units = (int)(H / EL);
     int rows[KMAX];
     float w[KMAX];
     token_entries<KMAX>(a, t, rows, w);
@@ -141,20 +156,20 @@ __device__ __forceinline__ void combine_item(const CombineArgs& a, int64_t t, in
         Unit<YF32> y[KMAX];
 #pragma unroll
         for (int k = 0; k < KMAX; ++k)
-            if (rows[k] >= 0) y[k].load(a.y, rows[k], H, (int64_t)u * 8);
-        float acc[8];
+            if (rows[k] >= 0) y[k].load(a.y, rows[k], H, (int64_t)u * EL);
+        float acc[EL];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+        for (int j = 0; j < EL; ++j) acc[j] = 0.0f;
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) {
             if (rows[k] < 0) continue;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
+            for (int j = 0; j < EL; ++j) {
                 const float p = w[k] * y[k].get(j);
                 acc[j] = acc[j] + p;
             }
         }
-        store_unit<OF32>(a.out, t, H, (int64_t)u * 8, acc);
+        store_unit<OF32, EL>(a.out, t, H, (int64_t)u * EL, acc);
     }
     if (c == 0 && threadIdx.x == 0 && a.out_weights) {
         float s = 0.0f;
@@ -254,7 +269,7 @@ __device__ __forceinline__ void combine_fp8_item(const CombineArgs& a, int64_t t
             float part[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) part[j] = acc[8 * h + j];
-            store_unit<OF32>(a.out, t, H, (int64_t)u * EL + 8 * h, part);
+            store_unit<OF32, 8>(a.out, t, H, (int64_t)u * EL + 8 * h, part);
         }
     }
     if (c == 0 && threadIdx.x == 0 && a.out_weights) {
@@ -340,8 +355,9 @@ __device__ __forceinline__ float dedup_weight_sum(const CombineArgs& a, const De
 
 template <bool YF32, bool OF32, int KMAX, int MODE>
 __device__ __forceinline__ void dedup_item(const CombineArgs& a, int64_t t, int c, int C) {
+    constexpr int EL = unit_elems(YF32);
     const int64_t H = a.H;
-    const int units = (int)(H / 8);
+    const int units = (int)(H / EL);
     DedupToken<KMAX> d;
     dedup_token<KMAX>(a, t, d);
 
@@ -351,38 +367,38 @@ __device__ __forceinline__ void dedup_item(const CombineArgs& a, int64_t t, int 
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) {
             y[k].clear();
-            if (d.rows[k] >= 0) y[k].load(a.y, d.rows[k], H, (int64_t)u * 8);
+            if (d.rows[k] >= 0) y[k].load(a.y, d.rows[k], H, (int64_t)u * EL);
         }
         // one wait for all K rows: the per-rank loop below uses them under
         // conditions and, in the two-stage form, stores between the uses
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) y[k].settle();
-        float acc[8];
+        float acc[EL];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+        for (int j = 0; j < EL; ++j) acc[j] = 0.0f;
         for (int r = 0; r < a.R; ++r) {
             const int rs = d.recv_row(r);
             if (rs < 0) continue;
-            float p[8];
+            float p[EL];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) p[j] = 0.0f;
+            for (int j = 0; j < EL; ++j) p[j] = 0.0f;
 #pragma unroll
             for (int k = 0; k < KMAX; ++k) {
                 if (d.rows[k] < 0 || d.ranks[k] != r) continue;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
+                for (int j = 0; j < EL; ++j) {
                     const float prod = d.w[k] * y[k].get(j);
                     p[j] = p[j] + prod;
                 }
             }
             if (MODE == 1) {
-                store_unit<true>(a.partial, rs, H, (int64_t)u * 8, p);
+                store_unit<true, EL>(a.partial, rs, H, (int64_t)u * EL, p);
             } else {
 #pragma unroll
-                for (int j = 0; j < 8; ++j) acc[j] = acc[j] + p[j];
+                for (int j = 0; j < EL; ++j) acc[j] = acc[j] + p[j];
             }
         }
-        if (MODE == 0) store_unit<OF32>(a.out, t, H, (int64_t)u * 8, acc);
+        if (MODE == 0) store_unit<OF32, EL>(a.out, t, H, (int64_t)u * EL, acc);
     }
     if (MODE == 0 && c == 0 && threadIdx.x == 0 && a.out_weights)
         a.out_weights[t] = dedup_weight_sum<KMAX>(a, d);
@@ -403,15 +419,16 @@ constexpr int kSumBatch = 8;
 
 template <bool OF32, int KMAX>
 __device__ __forceinline__ void dedup_sum_item(const CombineArgs& a, int64_t t, int c, int C) {
+    constexpr int EL = unit_elems(true);       // the partial rows are f32
     const int64_t H = a.H;
-    const int units = (int)(H / 8);
+    const int units = (int)(H / EL);
     DedupToken<KMAX> d;
     dedup_token<KMAX>(a, t, d);
     const int u = c * C + (int)threadIdx.x;
     if ((int)threadIdx.x < C && u < units) {
-        float acc[8];
+        float acc[EL];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+        for (int j = 0; j < EL; ++j) acc[j] = 0.0f;
         for (int r0 = 0; r0 < a.R; r0 += kSumBatch) {
             Unit<true> p[kSumBatch];
             int rs[kSumBatch];
@@ -419,7 +436,7 @@ __device__ __forceinline__ void dedup_sum_item(const CombineArgs& a, int64_t t, 
             for (int i = 0; i < kSumBatch; ++i) {
                 rs[i] = r0 + i < a.R ? d.recv_row(r0 + i) : -1;
                 p[i].clear();
-                if (rs[i] >= 0) p[i].load(a.partial, rs[i], H, (int64_t)u * 8);
+                if (rs[i] >= 0) p[i].load(a.partial, rs[i], H, (int64_t)u * EL);
             }
             // one wait for the batch instead of one per conditional use
 #pragma unroll
@@ -428,10 +445,10 @@ __device__ __forceinline__ void dedup_sum_item(const CombineArgs& a, int64_t t, 
             for (int i = 0; i < kSumBatch; ++i) {
                 if (rs[i] < 0) continue;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) acc[j] = acc[j] + p[i].get(j);
+                for (int j = 0; j < EL; ++j) acc[j] = acc[j] + p[i].get(j);
             }
         }
-        store_unit<OF32>(a.out, t, H, (int64_t)u * 8, acc);
+        store_unit<OF32, EL>(a.out, t, H, (int64_t)u * EL, acc);
     }
     if (c == 0 && threadIdx.x == 0 && a.out_weights) a.out_weights[t] = dedup_weight_sum<KMAX>(a, d);
 }
@@ -456,18 +473,20 @@ dim3 item_grid(int64_t items) {
 
 template <bool YF32, bool OF32, int KMAX>
 void plain_go(const CombineArgs& a, hipStream_t s) {
-    const Chunking ch = chunking(a.H);
+    const Chunking ch = chunking(a.H, unit_elems(YF32));
     combine_kernel<YF32, OF32, KMAX>
         <<<item_grid(a.T * ch.nch), dim3(threads_for(ch.C)), 0, s>>>(a, ch.C, ch.nch);
 }
 
 template <bool YF32, bool OF32, int KMAX>
 void dedup_go(const CombineArgs& a, hipStream_t s) {
-    const Chunking ch = chunking(a.H);
+    const Chunking ch = chunking(a.H, unit_elems(YF32));
     const dim3 grid = item_grid(a.T * ch.nch), block(threads_for(ch.C));
     if (a.partial) {
         dedup_combine_kernel<YF32, OF32, KMAX, 1><<<grid, block, 0, s>>>(a, ch.C, ch.nch);
-        dedup_sum_kernel<OF32, KMAX><<<grid, block, 0, s>>>(a, ch.C, ch.nch);
+        const Chunking cs = chunking(a.H, unit_elems(true));
+        dedup_sum_kernel<OF32, KMAX>
+            <<<item_grid(a.T * cs.nch), dim3(threads_for(cs.C)), 0, s>>>(a, cs.C, cs.nch);
     } else {
         dedup_combine_kernel<YF32, OF32, KMAX, 0><<<grid, block, 0, s>>>(a, ch.C, ch.nch);
     }
