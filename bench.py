@@ -649,8 +649,8 @@ def main():
         return
 
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
-              "sharding of this path is described in DESIGN.md and is not built.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this path is built "
+              "and measured on a single GPU; its multi-GPU form is not built.", file=sys.stderr)
         sys.exit(2)
 
     import torch
