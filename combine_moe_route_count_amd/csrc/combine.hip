@@ -47,11 +47,19 @@ struct Unit<false> {  // bf16: one 16-byte load
     __device__ __forceinline__ float get(int j) const {
         return (j & 1) ? bf16hi(a[j >> 1]) : bf16lo(a[j >> 1]);
     }
+    // the same, widened where it is used: inside a loop the compiler would
+    // otherwise widen every row once, before the loop, and keep 8 floats per row
+    __device__ __forceinline__ float get_here(int j) const {
+        uint32_t w = a[j >> 1];
+        asm volatile("" : "+v"(w));
+        return (j & 1) ? bf16hi(w) : bf16lo(w);
+    }
 };
 
 template <>
 struct Unit<true> {  // f32: one 16-byte load
     u32x4 a;
+    __device__ __forceinline__ float get_here(int j) const { return get(j); }
     __device__ __forceinline__ void clear() { a = u32x4{0, 0, 0, 0}; }
     __device__ __forceinline__ void settle() { asm volatile("" : "+v"(a)); }
     __device__ __forceinline__ void load(const void* y, int64_t row, int64_t H, int64_t col) {
@@ -387,7 +395,7 @@ __device__ __forceinline__ void dedup_item(const CombineArgs& a, int64_t t, int 
                 if (d.rows[k] < 0 || d.ranks[k] != r) continue;
 #pragma unroll
                 for (int j = 0; j < EL; ++j) {
-                    const float prod = d.w[k] * y[k].get(j);
+                    const float prod = d.w[k] * y[k].get_here(j);
                     p[j] = p[j] + prod;
                 }
             }
