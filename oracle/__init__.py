@@ -52,12 +52,17 @@ def build(verbose: bool = False) -> str:
 
 
 def _load():
+    """The compiled oracle; MOE_ORACLE_LIB names another build of the same
+    source (the sanitizer test loads one built with ASan and UBSan)."""
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
-        build()
-    lib = ctypes.CDLL(_LIB_PATH)
+    path = os.environ.get("MOE_ORACLE_LIB")
+    if not path:
+        path = _LIB_PATH
+        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_SRC):
+            build()
+    lib = ctypes.CDLL(path)
     P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     sigs = {
         "oracle_route_count": [P, I64, I32, I32, P, P, P],
