@@ -57,5 +57,27 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+C_SMOKE_SRC = os.path.join(ROOT, "tests", "c_abi_smoke.c")
+C_SMOKE_BIN = os.path.join(ROOT, "tests", "c_abi_smoke")
+
+
+def build_c_abi_smoke(verbose: bool = False) -> str:
+    """Compile the plain-C user of the ABI (tests/c_abi_smoke.c) against the
+    built library, with gcc: no HIP device code, only the runtime's C API."""
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(HIPCC)))
+    cmd = ["gcc", "-std=gnu99", "-O2", "-Wall", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(rocm, "include"), "-I", os.path.join(ROOT, "include"),
+           C_SMOKE_SRC, "-o", C_SMOKE_BIN, "-L", HERE, "-lmoe_route",
+           "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN/../combine_moe_route_count_amd",
+           "-Wl,-rpath," + os.path.join(rocm, "lib")]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"gcc failed for {C_SMOKE_SRC}:\n{r.stdout}\n{r.stderr}")
+    return C_SMOKE_BIN
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))

@@ -996,3 +996,17 @@ def test_soak_random_T():
             eo, ew = oracle.combine(ref["packed"], "bf16", ref["tok_map"], w, "bf16")
         _check_combine(host(out[:T]), eo, "bf16")
         np.testing.assert_array_equal(host(ow[:T]).view(np.uint32), ew.view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# the ABI from plain C (no Python, no torch): tests/c_abi_smoke.c, built by build()
+# ---------------------------------------------------------------------------
+
+def test_c_abi_program():
+    import os
+    import subprocess
+    exe = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c_abi_smoke")
+    assert os.path.exists(exe), "tests/c_abi_smoke is missing: run __graft_entry__.build()"
+    note("c abi smoke program")
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and "c abi smoke: ok" in r.stdout, (r.returncode, r.stdout, r.stderr)
