@@ -74,7 +74,17 @@
 extern "C" {
 #endif
 
-typedef enum { MOE_BF16 = 0, MOE_F32 = 1, MOE_FP8_E4M3 = 2, MOE_FP4_E2M1 = 3 } moe_dtype;
+/* The two range markers make every int a value of the type (in C++ too, where
+ * an enum holds only the values its enumerators span): a caller may pass any
+ * code, and an unknown one is rejected with MOE_ERR_INVALID_ARG. */
+typedef enum {
+    MOE_BF16 = 0,
+    MOE_F32 = 1,
+    MOE_FP8_E4M3 = 2,
+    MOE_FP4_E2M1 = 3,
+    MOE_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+    MOE_DTYPE_RANGE_MAX_ = 2147483647
+} moe_dtype;
 
 typedef enum {
     MOE_OK = 0,
