@@ -496,11 +496,25 @@ dim3 item_grid(int64_t items) {
     return dim3((unsigned)(items < kMaxGrid ? items : kMaxGrid));
 }
 
+// Residency cap of the bf16 gather.  At the 8 workgroups per CU its registers
+// allow, the gather keeps about 64 MB of row loads in flight chip-wide and
+// HBM delivers less (181 us for the 1.06 GB combine at T=8192 H=7168 K=8);
+// at 4 or 5 per CU (32-40 MB in flight) the same launch takes 173 us, at 3 per
+// CU 185 us.  The launch reserves LDS it never touches so that at most
+// kGatherWgsPerCu workgroups share a CU's 160 KB.  The f32-row dedup forms
+// lost time under the same cap (fused dedup combine 321 -> 356 us), and so did
+// the quantized combines, whose dequantize needs the VALU latency hiding of
+// full residency (e4m3 104 -> 131 us); those launch uncapped.
+constexpr size_t kLdsPerCu = 160 * 1024;   // gfx950
+constexpr int kGatherWgsPerCu = 5;
+constexpr size_t kGatherLdsReserve = kLdsPerCu / kGatherWgsPerCu;
+
 template <bool YF32, bool OF32, int KMAX>
 void plain_go(const CombineArgs& a, hipStream_t s) {
     const Chunking ch = chunking(a.H, unit_elems(YF32));
+    const size_t lds = YF32 ? 0 : kGatherLdsReserve;
     combine_kernel<YF32, OF32, KMAX>
-        <<<item_grid(a.T * ch.nch), dim3(threads_for(ch.C)), 0, s>>>(a, ch.C, ch.nch);
+        <<<item_grid(a.T * ch.nch), dim3(threads_for(ch.C)), lds, s>>>(a, ch.C, ch.nch);
 }
 
 template <bool YF32, bool OF32, int KMAX>
