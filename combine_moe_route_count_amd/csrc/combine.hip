@@ -505,7 +505,6 @@ dim3 item_grid(int64_t items) {
 // lost time under the same cap (fused dedup combine 321 -> 356 us), and so did
 // the quantized combines, whose dequantize needs the VALU latency hiding of
 // full residency (e4m3 104 -> 131 us); those launch uncapped.
-constexpr size_t kLdsPerCu = 160 * 1024;   // gfx950
 constexpr int kGatherWgsPerCu = 5;
 constexpr size_t kGatherLdsReserve = kLdsPerCu / kGatherWgsPerCu;
 

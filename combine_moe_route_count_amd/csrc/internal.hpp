@@ -114,6 +114,11 @@ hipError_t launch_expand(const ExpandArgs& a, hipStream_t s);
 // 16 waves x NK running counts in LDS.
 constexpr int kFusedMaxKeys = 512;
 
+// LDS of one gfx950 CU.  Launches that cap their residency reserve
+// kLdsPerCu / n bytes of LDS per workgroup (never touched), so that at most n
+// of their workgroups share a CU.
+constexpr size_t kLdsPerCu = 160 * 1024;
+
 struct RouteFusedArgs {
     KeyKind kind;
     const int32_t* idx;

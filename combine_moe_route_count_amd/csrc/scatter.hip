@@ -30,8 +30,11 @@ constexpr int kCopyThreads = 256;
 // cached tok_map, taken as they stand when inside [0, packed_rows) (nothing is
 // written back); otherwise the routing lookup, which also writes tok_map and
 // packed_src.
+// meta: this workgroup writes tok_map and packed_src (one workgroup per token
+// does when the row is split over several).
 template <int DMAX, bool REPLAY>
-__device__ __forceinline__ void token_rows(const ScatterArgs& a, int64_t t, int (&rows)[DMAX]) {
+__device__ __forceinline__ void token_rows(const ScatterArgs& a, int64_t t, int (&rows)[DMAX],
+                                           bool meta = true) {
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
     const int K = a.slot.K;
@@ -43,7 +46,7 @@ __device__ __forceinline__ void token_rows(const ScatterArgs& a, int64_t t, int 
         }
     } else {
         if (lane < K) my_row = entry_row(a.slot, t * K + lane);
-        if (tid < K) {
+        if (tid < K && meta) {
             a.tok_map[t * K + tid] = my_row;
             if (my_row >= 0) a.packed_src[my_row] = (int32_t)t;
         }
@@ -93,12 +96,16 @@ __device__ __forceinline__ void scatter_copy_kernel_item(const ScatterArgs& a, i
 // plain dispatch, fused blockwise fp8 pack (bf16 in)
 // ---------------------------------------------------------------------------
 
+// Units [c*C, c*C + C) of token t's row (C a multiple of the 8 units of a
+// scale block); chunk 0 also writes the token's tok_map and packed_src.
 template <int DMAX, int UPT, bool REPLAY, bool FP4>
-__device__ __forceinline__ void scatter_fp8_kernel_item(const ScatterArgs& a, int64_t t, int nth) {
+__device__ __forceinline__ void scatter_fp8_kernel_item(const ScatterArgs& a, int64_t t, int nth,
+                                                        int c, int C) {
     const int tid = threadIdx.x;
     const int K = a.slot.K;
     const int64_t H = a.H;
-    const int nunits = (int)(H / 16);          // 16 elements per lane-unit
+    const int u0 = c * C;
+    const int nunits = min((int)(H / 16), u0 + C);   // 16 elements per lane-unit; chunk end
     const int64_t nblk = H / kFp8Block;
     const int step = UPT * nth;
     const char* src = (const char*)a.x + t * H * 2;
@@ -107,7 +114,7 @@ __device__ __forceinline__ void scatter_fp8_kernel_item(const ScatterArgs& a, in
     u32x4 lo[UPT], hi[UPT];
 #pragma unroll
     for (int i = 0; i < UPT; ++i) {
-        const int u = tid + i * nth;
+        const int u = u0 + tid + i * nth;
         lo[i] = u32x4{0, 0, 0, 0};
         hi[i] = u32x4{0, 0, 0, 0};
         if (u < nunits) {
@@ -117,9 +124,9 @@ __device__ __forceinline__ void scatter_fp8_kernel_item(const ScatterArgs& a, in
     }
 
     int rows[DMAX];
-    token_rows<DMAX, REPLAY>(a, t, rows);
+    token_rows<DMAX, REPLAY>(a, t, rows, c == 0);
     const int64_t prow = FP4 ? H / 2 : H;      // bytes per packed row
-    for (int base = 0;;) {
+    for (int base = u0;;) {
         u32x4 q[UPT];
         u32x2 q4[UPT];
         float s[UPT];
@@ -289,9 +296,13 @@ __global__ __launch_bounds__(kCopyThreads) void scatter_copy_kernel(ScatterArgs 
         scatter_copy_kernel_item<DMAX, VPT, REPLAY, SC>(a, t, nth);
 }
 template <int DMAX, int UPT, bool REPLAY, bool FP4>
-__global__ __launch_bounds__(kCopyThreads) void scatter_fp8_kernel(ScatterArgs a, int nth) {
-    for (int64_t t = blockIdx.x; t < a.T; t += gridDim.x)
-        scatter_fp8_kernel_item<DMAX, UPT, REPLAY, FP4>(a, t, nth);
+__global__ __launch_bounds__(kCopyThreads) void scatter_fp8_kernel(ScatterArgs a, int nth, int nch,
+                                                                   int C) {
+    const int64_t items = a.T * nch;
+    for (int64_t wi = blockIdx.x; wi < items; wi += gridDim.x) {
+        const int64_t t = wi / nch;
+        scatter_fp8_kernel_item<DMAX, UPT, REPLAY, FP4>(a, t, nth, (int)(wi - t * nch), C);
+    }
 }
 template <int DMAX, int VPT>
 __global__ __launch_bounds__(kCopyThreads) void recv_copy_kernel(RecvArgs a, int nth) {
@@ -385,6 +396,34 @@ hipError_t by_dmax(int D, dim3 grid, int threads, const Args& a, hipStream_t s) 
     return hipGetLastError();
 }
 
+// Split of a token row over the workgroups of the quantizing scatter.  The
+// e4m3 forms give each token two workgroups (half a row each) and cap the
+// launch at 8 workgroups per CU through an LDS reservation: fewer rows are
+// being written at any moment, and HBM takes the writes faster (the
+// T=8192 H=7168 K=8 skewed dispatch: 123 -> 120 us; one workgroup per token
+// capped at 3 per CU 120-122 us; four per token 125-127 us).  The e2m1 form,
+// half the bytes per row, lost time under the same cap (79.5 -> 82.5 us) and
+// keeps one uncapped workgroup per token.
+struct Fp8Split {
+    int nch;       // workgroups per token
+    int C;         // lane-units per workgroup, a multiple of a scale block's 8
+    int threads;
+    size_t lds;
+};
+constexpr int kFp8SplitChunks = 2;
+constexpr int kFp8SplitWgsPerCu = 8;
+
+inline Fp8Split fp8_split(int64_t H, bool fp4) {
+    const int nunits = (int)(H / 16);
+    const int nblk = nunits / 8;
+    Fp8Split sp;
+    sp.nch = fp4 ? 1 : (nblk < kFp8SplitChunks ? nblk : kFp8SplitChunks);
+    sp.C = ((nblk + sp.nch - 1) / sp.nch) * 8;
+    sp.threads = copy_threads<2>(sp.C);
+    sp.lds = fp4 ? 0 : kLdsPerCu / kFp8SplitWgsPerCu;
+    return sp;
+}
+
 template <bool REPLAY, bool SC>
 struct CopyMode {
     template <int D, int V>
@@ -398,8 +437,12 @@ template <bool REPLAY, bool FP4>
 struct Fp8Mode {
     template <int D, int V>
     struct Launch {
-        static void go(dim3 g, int th, const ScatterArgs& a, hipStream_t s) {
-            scatter_fp8_kernel<D, V, REPLAY, FP4><<<g, dim3(th), 0, s>>>(a, th);
+        static void go(dim3, int, const ScatterArgs& a, hipStream_t s) {
+            const Fp8Split sp = fp8_split(a.H, FP4);
+            const int64_t items = a.T * sp.nch;
+            const dim3 grid((unsigned)(items < kMaxGrid ? items : kMaxGrid));
+            scatter_fp8_kernel<D, V, REPLAY, FP4>
+                <<<grid, dim3(sp.threads), sp.lds, s>>>(a, sp.threads, sp.nch, sp.C);
         }
     };
 };
@@ -422,8 +465,7 @@ hipError_t launch_scatter(const ScatterArgs& a, hipStream_t s) {
     if (a.T == 0) return hipSuccess;
     const dim3 grid((unsigned)(a.T < kMaxGrid ? a.T : kMaxGrid));
     if (a.fp8) {
-        const int nunits = (int)(a.H / 16);
-        const int th = copy_threads<2>(nunits);
+        const int th = 0;   // Fp8Mode sizes its own launch (fp8_split)
         if (a.fp4)
             return a.replay ? by_dmax<Fp8Mode<true, true>::Launch, 2>(a.slot.K, grid, th, a, s)
                             : by_dmax<Fp8Mode<false, true>::Launch, 2>(a.slot.K, grid, th, a, s);

@@ -707,6 +707,27 @@ def test_dispatch_fp4_small(layout, T, K, E, H):
     assert_dispatch_equal(o, ref, fp8=True)
 
 
+# The e4m3 scatter splits each token row over two workgroups of whole scale
+# blocks: one block (no split), an odd block count (uneven halves), and halves
+# wider than one pass of the workgroup (H=16512: 65 blocks per half).
+@pytest.mark.parametrize("layout", ["compact", "padded_tight", "compact_short"])
+@pytest.mark.parametrize("T,K,E,H", [(300, 4, 13, 128), (2100, 8, 256, 384), (257, 8, 64, 7296),
+                                     (97, 3, 7, 16512)])
+def test_dispatch_fp8_small(layout, T, K, E, H):
+    rng = np.random.default_rng(T + K * 5 + H)
+    idx = _mixed_idx(rng, T, K, E)
+    x = W.inject_outliers(W.normal_x(rng, T, H, "bf16"), np.arange(0, T, 13), 1000.0)
+    flat = idx.ravel()
+    cnt = np.bincount(flat[(flat >= 0) & (flat < E)], minlength=E)
+    cap = {"compact": 0, "padded_tight": max(1, int(cnt.max()) // 2), "compact_short": 0}[layout]
+    rows = {"compact": T * K, "padded_tight": E * cap - 3,
+            "compact_short": max(0, int(cnt.sum()) - 37)}[layout]
+    note(f"dispatch fp8 {layout} T={T} K={K} E={E} H={H}")
+    o = gpu_dispatch(dev_bf16(x), idx, E, cap=cap, packed_rows=rows, fp8=True)
+    ref = oracle.dispatch(x, "bf16", idx, E, cap=cap, packed_rows=rows, packed_dt="fp8")
+    assert_dispatch_equal(o, ref, fp8=True)
+
+
 @pytest.mark.parametrize("out_dt", ["bf16", "f32"])
 @pytest.mark.parametrize("K,H,T,scaled", [(1, 128, 37, True), (3, 384, 300, False), (8, 7168, 129, True),
                                           (16, 256, 513, True)])
