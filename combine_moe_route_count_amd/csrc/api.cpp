@@ -540,6 +540,10 @@ MOE_API int moe_dedup_dispatch(const void* x, moe_dtype x_dt, int64_t T, int64_t
     rc.recv_x = recv_x;
     rc.recv_src = recv_src;
     rc.rank_slot = rank_slot;
+    rc.idx = idx;
+    rc.K = K;
+    rc.E = E;
+    rc.tok_map = tok_map;
     MOE_HIP(moe::launch_recv_copy(rc, s), "moe_dedup_dispatch recv copy");
 
     // stage 2 routing: surviving entries to expert slots, then local expansion
@@ -556,7 +560,9 @@ MOE_API int moe_dedup_dispatch(const void* x, moe_dtype x_dt, int64_t T, int64_t
     ea.H = H;
     ea.x_bytes = xb;
     ea.R = R;
-    ea.rank_slot = rank_slot;
+    ea.recv_src = recv_src;
+    ea.recv_off = at<int32_t>(ws, L.ranks.off);
+    ea.recv_rows = recv_rows;
     ea.recv_x = recv_x;
     ea.packed = packed_x;
     ea.packed_src = packed_src;

@@ -90,6 +90,9 @@ struct RecvArgs {             // dedup stage 1: one copy per (token, rank)
     void* recv_x;
     int32_t* recv_src;
     int32_t* rank_slot;
+    const int32_t* idx;         // [T,K] expert ids: entries with no recv row get tok_map -1 here
+    int K, E;
+    int64_t* tok_map;
 };
 hipError_t launch_recv_copy(const RecvArgs& a, hipStream_t s);
 
@@ -98,7 +101,9 @@ struct ExpandArgs {           // dedup stage 2: recv rows -> per-expert rows
     int64_t T, H;
     int x_bytes;
     int R;
-    const int32_t* rank_slot;
+    const int32_t* recv_src;    // [recv_rows] token of each recv row
+    const int32_t* recv_off;    // [R+1] rank segments of the recv rows (uncapped counts)
+    int64_t recv_rows;
     const void* recv_x;
     void* packed;
     int32_t* packed_src;
