@@ -362,13 +362,22 @@ def test_dedup_workload_full():
     plain = oracle.dispatch(d["x"], "f32", d["idx"], E)
     np.testing.assert_array_equal(host(o.tok_map), plain["tok_map"])
     rr = T * min(K, R)
-    plan = dict(R=R, idx=dev(d["idx"]), rank_slot=o.rank_slot, recv_rows=rr)
-    out, ow = moe.combine(o.packed, o.tok_map, dev(d["w"]), E=E, out_dtype=torch.float32, dedup=plan)
-    torch.cuda.synchronize()
-    eo, ew, _ = oracle.dedup_combine(ref["packed"], "f32", ref["tok_map"], d["w"], d["idx"], E, R,
-                                     ref["rank_slot"], rr, "f32")
-    _check_combine(host(out), eo, "f32")
-    np.testing.assert_array_equal(host(ow), ew)
+    eo, ew, ep = oracle.dedup_combine(ref["packed"], "f32", ref["tok_map"], d["w"], d["idx"], E, R,
+                                      ref["rank_slot"], rr, "f32", want_partial=True)
+    # fused (partials in registers) and two-stage (partial rows through memory)
+    for with_partial in (False, True):
+        part = torch.empty((rr, H), dtype=torch.float32, device=DEV) if with_partial else None
+        poison_(part)
+        plan = dict(R=R, idx=dev(d["idx"]), rank_slot=o.rank_slot, recv_rows=rr, partial=part)
+        out, ow = moe.combine(o.packed, o.tok_map, dev(d["w"]), E=E, out_dtype=torch.float32,
+                              dedup=plan)
+        torch.cuda.synchronize()
+        _check_combine(host(out), eo, "f32")
+        np.testing.assert_array_equal(host(ow), ew)
+        if with_partial:
+            n = int(ref["recv_off"][R])
+            np.testing.assert_array_equal(host(part)[:n].view(np.uint32), ep[:n].view(np.uint32))
+        del part
 
 
 # ---------------------------------------------------------------------------
