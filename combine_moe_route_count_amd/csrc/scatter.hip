@@ -2,7 +2,8 @@
 // packed rows (bit copies or the fused blockwise fp8 pack), the dedup recv copy
 // and local expansion, and the fp8 dequantize helper.
 //
-// One workgroup per source token.  The token row is loaded once into
+// One workgroup per source token (the e4m3 pack: two, half a row each; the
+// dedup expansion: one per recv row).  The token row is loaded once into
 // registers with 16-byte loads (issued before the routing lookups, whose
 // latency they hide), then stored to each of the token's destination rows with
 // 16-byte stores, as the byte-generic row copy of "Draft: cco + flydsl
@@ -259,7 +260,7 @@ __device__ __forceinline__ void expand_kernel_item(const ExpandArgs& a, int64_t 
 }
 
 // ---------------------------------------------------------------------------
-// kernels: one source token per workgroup, grid-stride over tokens
+// kernels: grid-stride over their work items (tokens, token halves or recv rows)
 // ---------------------------------------------------------------------------
 // nth is the workgroup size, passed as an argument: blockDim.x comes from a
 // 16-bit field that gfx9 can only read with a vector load, which the compiler
