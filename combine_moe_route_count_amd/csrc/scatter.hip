@@ -200,8 +200,8 @@ __device__ __forceinline__ void recv_copy_kernel_item(const RecvArgs& a, int64_t
     // rows, writes every other entry.  Rank of a valid e: e / (E/R).
     {
         int e = -1;
-        if (lane < a.K) e = a.idx[t * a.K + lane];
-        const bool valid = lane < a.K && e >= 0 && e < a.E;
+        if (tid < a.K) e = a.idx[t * a.K + tid];
+        const bool valid = tid < a.K && e >= 0 && e < a.E;
         const int rk = valid ? e / (a.E / R) : 0;
         const int rs = __shfl(my_row, rk, kWave);
         if (tid < a.K && (!valid || rs < 0)) a.tok_map[t * a.K + tid] = -1;
@@ -244,14 +244,20 @@ __device__ __forceinline__ void expand_kernel_item(const ExpandArgs& a, int64_t 
     const int32_t t = a.recv_src[j];
 
     int my_row = -1;
-    if (lane < K && t >= 0 && t < a.T) {
+    bool on_rank = false;   // this lane's entry belongs to row j's rank
+    if (lane < K && r >= 0 && t >= 0 && t < a.T) {
         const int64_t f = (int64_t)t * K + lane;
         const int32_t e = a.slot.idx[f];
-        if (r >= 0 && e >= 0 && e < a.slot.E && e / er == r) {
+        if (e >= 0 && e < a.slot.E && e / er == r) {
+            on_rank = true;
             my_row = entry_row(a.slot, f);
-            a.tok_map[f] = my_row;
-            if (my_row >= 0) a.packed_src[my_row] = t;
         }
+    }
+    // every wave needs the rows for its broadcast; the first wave writes them
+    if (tid < K && on_rank) {
+        const int64_t f = (int64_t)t * K + tid;
+        a.tok_map[f] = my_row;
+        if (my_row >= 0) a.packed_src[my_row] = t;
     }
     int rows[KMAX];
     broadcast_rows<KMAX>(my_row, rows);
