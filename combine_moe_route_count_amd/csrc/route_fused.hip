@@ -62,14 +62,20 @@ __global__ __launch_bounds__(kFusedThreads) void route_fused_kernel(KeyFn keys, 
     // kernel's streaming stores fill, and measured about 10 us per launch.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (tid == 0) s_last = arrive_ticket(a.ticket) == (uint32_t)a.scan.tiles;
-    __syncthreads();
-    if (!s_last) return;
+    // A launch of one tile (up to 1024 entries: the decode-sized calls) is its
+    // own last workgroup: it scans right away and leaves the ticket alone,
+    // saving the arrival's round trip.
+    const bool single = a.scan.tiles == 1;
+    if (!single) {
+        if (tid == 0) s_last = arrive_ticket(a.ticket) == (uint32_t)a.scan.tiles;
+        __syncthreads();
+        if (!s_last) return;
+    }
     // Every tile's counts are at the coherence point (agent-scope stores that
     // completed before their ticket arrivals, which precede this one); the scan
     // reads them with agent-scope loads, so no cache invalidate is needed.
     scan_tiles_body<true>(a.scan);
-    if (tid == 0)
+    if (tid == 0 && !single)
         __hip_atomic_store(a.ticket, (uint64_t)kTicketTag << 32, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
 }
