@@ -55,12 +55,16 @@ struct SurvivorKeys {
 // equal-key lanes below it (mbcnt) plus the wave's running count in LDS, and
 // after a barrier each entry adds the counts of the tile's earlier waves.
 // run_all: LDS of WAVES*NK ints.  All threads of the workgroup must call it.
+// flags_lds (optional, LDS): the workgroup scans its own tile (a one-tile
+// launch), so nothing is published: thread 0 leaves the two flag totals there
+// and the counts stay in run_all.
 template <int WAVES, int CHUNKS, class KeyFn>
 __device__ __forceinline__ void rank_tile(const KeyFn& keys, int64_t N, int NK, int nbits,
                                           int64_t tile, int32_t* run_all,
                                           int32_t* __restrict__ local_rank,
                                           int32_t* __restrict__ tile_cnt,
-                                          int32_t* __restrict__ tile_flags) {
+                                          int32_t* __restrict__ tile_flags,
+                                          int32_t* flags_lds = nullptr) {
     static_assert(WAVES * CHUNKS * kWave == kTile, "tile size");
     __shared__ int32_t flag_cnt[WAVES][2];
     const int tid = threadIdx.x;
@@ -112,11 +116,14 @@ __device__ __forceinline__ void rank_tile(const KeyFn& keys, int64_t N, int NK, 
     // possibly in the same launch on another XCD: agent-scope stores write
     // them through to the device coherence point, so the publisher only has to
     // wait for their completion instead of writing back its whole L2.
-    for (int e = tid; e < NK; e += WAVES * kWave) {
-        int s = 0;
+    if (!flags_lds) {
+        for (int e = tid; e < NK; e += WAVES * kWave) {
+            int s = 0;
 #pragma unroll
-        for (int w = 0; w < WAVES; ++w) s += run_all[w * NK + e];
-        __hip_atomic_store(&tile_cnt[tile * NK + e], s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int w = 0; w < WAVES; ++w) s += run_all[w * NK + e];
+            __hip_atomic_store(&tile_cnt[tile * NK + e], s, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
     if (tid == 0) {
         int a = 0, b = 0;
@@ -125,9 +132,15 @@ __device__ __forceinline__ void rank_tile(const KeyFn& keys, int64_t N, int NK, 
             a += flag_cnt[w][0];
             b += flag_cnt[w][1];
         }
-        __hip_atomic_store(&tile_flags[2 * tile], a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&tile_flags[2 * tile + 1], b, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+        if (flags_lds) {
+            flags_lds[0] = a;
+            flags_lds[1] = b;
+        } else {
+            __hip_atomic_store(&tile_flags[2 * tile], a, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&tile_flags[2 * tile + 1], b, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
 }
 
@@ -174,9 +187,18 @@ __device__ __forceinline__ int32_t ld_count(const int32_t* p) {
 // [t0, t1) of one key: it loads their counts once (all loads issued together),
 // sums them, takes the prefix of the earlier parts from LDS and writes the
 // exclusive tile bases.  The per-key totals are then scanned over keys for the
-// offsets.
+// offsets.  one_tile (optional): a single-tile launch scanned by the workgroup
+// that ranked it, whose counts are still in its LDS (one_tile->run: waves x NK
+// running counts; one_tile->flags: the two flag totals), so nothing is read back
+// from memory.
+struct OneTileLds {
+    const int32_t* run;
+    int waves;
+    const int32_t* flags;
+};
 template <bool COHERENT>
-__device__ __forceinline__ void scan_tiles_body(const ScanArgs& a) {
+__device__ __forceinline__ void scan_tiles_body(const ScanArgs& a,
+                                                const OneTileLds* one_tile = nullptr) {
     __shared__ int32_t part_sum[kScanThreads];
     __shared__ int32_t key_total[kScanThreads];
     __shared__ int32_t wave_sums[kScanThreads / kWave];
@@ -197,15 +219,26 @@ __device__ __forceinline__ void scan_tiles_body(const ScanArgs& a) {
 
     int32_t c[kScanCache];
     int32_t s = 0;
-#pragma unroll
-    for (int i = 0; i < kScanCache; ++i) {
-        const int tl = t0 + i;
-        c[i] = (active && tl < t1) ? ld_count<COHERENT>(&a.tile_cnt[(int64_t)tl * NK + key]) : 0;
-    }
     int32_t fi = 0, fd = 0;
-    for (int tl = tid; tl < tiles; tl += kScanThreads) {
-        fi += ld_count<COHERENT>(&a.tile_flags[2 * (int64_t)tl]);
-        fd += ld_count<COHERENT>(&a.tile_flags[2 * (int64_t)tl + 1]);
+    if (one_tile) {   // tiles == 1, parts == 1: thread key sums its key over the waves
+#pragma unroll
+        for (int i = 0; i < kScanCache; ++i) c[i] = 0;
+        if (active)
+            for (int w = 0; w < one_tile->waves; ++w) c[0] += one_tile->run[w * NK + key];
+        if (tid == 0) {
+            fi = one_tile->flags[0];
+            fd = one_tile->flags[1];
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kScanCache; ++i) {
+            const int tl = t0 + i;
+            c[i] = (active && tl < t1) ? ld_count<COHERENT>(&a.tile_cnt[(int64_t)tl * NK + key]) : 0;
+        }
+        for (int tl = tid; tl < tiles; tl += kScanThreads) {
+            fi += ld_count<COHERENT>(&a.tile_flags[2 * (int64_t)tl]);
+            fd += ld_count<COHERENT>(&a.tile_flags[2 * (int64_t)tl + 1]);
+        }
     }
 #pragma unroll
     for (int i = 0; i < kScanCache; ++i) s += c[i];

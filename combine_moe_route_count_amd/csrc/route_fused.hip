@@ -52,9 +52,21 @@ template <class KeyFn>
 __global__ __launch_bounds__(kFusedThreads) void route_fused_kernel(KeyFn keys, RouteFusedArgs a) {
     extern __shared__ int32_t run_all[];  // [kFusedWaves][NK] routing counts
     __shared__ uint32_t s_last;
+    __shared__ int32_t tile_flags_lds[2];
     const int tid = threadIdx.x;
+    // A launch of one tile (up to 1024 entries: the decode-sized calls) is its
+    // own last workgroup: it scans its counts straight from LDS, with no wait
+    // for its stores, no ticket and no read back.
+    const bool single = a.scan.tiles == 1;
     rank_tile<kFusedWaves, 1>(keys, a.N, a.scan.NK, a.nbits, (int64_t)blockIdx.x, run_all,
-                              a.local_rank, a.scan.tile_cnt, (int32_t*)a.scan.tile_flags);
+                              a.local_rank, a.scan.tile_cnt, (int32_t*)a.scan.tile_flags,
+                              single ? tile_flags_lds : nullptr);
+    if (single) {
+        __syncthreads();
+        const OneTileLds lds{run_all, kFusedWaves, tile_flags_lds};
+        scan_tiles_body<true>(a.scan, &lds);
+        return;
+    }
     // Publication of the tile: its counts and flags were stored at agent scope
     // (written through to the coherence point), so completing them is enough
     // for the last workgroup to see them; an agent-scope release fence would
@@ -62,20 +74,14 @@ __global__ __launch_bounds__(kFusedThreads) void route_fused_kernel(KeyFn keys, 
     // kernel's streaming stores fill, and measured about 10 us per launch.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    // A launch of one tile (up to 1024 entries: the decode-sized calls) is its
-    // own last workgroup: it scans right away and leaves the ticket alone,
-    // saving the arrival's round trip.
-    const bool single = a.scan.tiles == 1;
-    if (!single) {
-        if (tid == 0) s_last = arrive_ticket(a.ticket) == (uint32_t)a.scan.tiles;
-        __syncthreads();
-        if (!s_last) return;
-    }
+    if (tid == 0) s_last = arrive_ticket(a.ticket) == (uint32_t)a.scan.tiles;
+    __syncthreads();
+    if (!s_last) return;
     // Every tile's counts are at the coherence point (agent-scope stores that
     // completed before their ticket arrivals, which precede this one); the scan
     // reads them with agent-scope loads, so no cache invalidate is needed.
     scan_tiles_body<true>(a.scan);
-    if (tid == 0 && !single)
+    if (tid == 0)
         __hip_atomic_store(a.ticket, (uint64_t)kTicketTag << 32, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
 }
