@@ -148,10 +148,8 @@ struct LevelOut {
     int32_t* stats = nullptr;
 };
 
-hipError_t route_level(void* ws, const RouteWs& L, size_t ticket, moe::KeyKind kind,
-                       const int32_t* idx, const int32_t* rank_slot, int64_t N, int K, int E,
-                       int R, int NK, int64_t cap, int64_t rows_limit, const LevelOut& o,
-                       moe::StatsMode mode, hipStream_t s) {
+moe::ScanArgs scan_args(void* ws, const RouteWs& L, int NK, int64_t cap, int64_t rows_limit,
+                        const LevelOut& o, moe::StatsMode mode) {
     moe::ScanArgs sa;
     sa.tile_cnt = at<int32_t>(ws, L.tile_cnt);
     sa.tile_flags = at<int32_t>(ws, L.tile_flags);
@@ -166,6 +164,14 @@ hipError_t route_level(void* ws, const RouteWs& L, size_t ticket, moe::KeyKind k
     sa.packed_off = o.packed_off;
     sa.stats = o.stats;
     sa.mode = mode;
+    return sa;
+}
+
+hipError_t route_level(void* ws, const RouteWs& L, size_t ticket, moe::KeyKind kind,
+                       const int32_t* idx, const int32_t* rank_slot, int64_t N, int K, int E,
+                       int R, int NK, int64_t cap, int64_t rows_limit, const LevelOut& o,
+                       moe::StatsMode mode, hipStream_t s) {
+    const moe::ScanArgs sa = scan_args(ws, L, NK, cap, rows_limit, o, mode);
     int nbits = 0;
     while ((1 << nbits) < NK) ++nbits;
     if (L.tiles > 0 && NK <= moe::kFusedMaxKeys) {
@@ -324,6 +330,12 @@ int dispatch_impl(const void* x, moe_dtype x_dt, const float* x_scales, int64_t 
     o.packed_cnt = packed_cnt;
     o.packed_off = packed_off;
     o.stats = stats;
+    if (moe::dispatch_small_fits(T, K, E)) {   // one routing tile: routing and scatter in one launch
+        MOE_HIP(moe::launch_dispatch_small(
+                    sa, scan_args(ws, L.experts, E, cap, packed_rows, o, moe::StatsMode::Plain), s),
+                "dispatch (one launch)");
+        return ok();
+    }
     MOE_HIP(route_level(ws, L.experts, L.ticket, moe::KeyKind::Experts, idx, nullptr, T * K, K, E,
                         0, E, cap, packed_rows, o, moe::StatsMode::Plain, s),
             "dispatch routing");

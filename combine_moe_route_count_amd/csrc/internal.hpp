@@ -78,6 +78,12 @@ struct ScatterArgs {
 };
 hipError_t launch_scatter(const ScatterArgs& a, hipStream_t s);
 
+// Routing and scatter of a dispatch in one launch when its routing is one tile
+// and its keys fit the one-launch routing (dispatch_small_fits); sc is the
+// routing's scan description (outputs, limits) as for the two-launch path.
+bool dispatch_small_fits(int64_t T, int K, int E);
+hipError_t launch_dispatch_small(const ScatterArgs& a, const ScanArgs& sc, hipStream_t s);
+
 struct RecvArgs {             // dedup stage 1: one copy per (token, rank)
     const void* x;
     int64_t T, H;

@@ -16,6 +16,7 @@
 // bytes with one 16-byte store.
 #include "device_common.hpp"
 #include "internal.hpp"
+#include "route_device.hpp"
 #include "rows_device.hpp"
 
 namespace moe {
@@ -72,8 +73,22 @@ __device__ __forceinline__ void forward_scales(const ScatterArgs& a, int64_t t, 
     }
 }
 
-template <int DMAX, int VPT, bool REPLAY, bool SC>
-__device__ __forceinline__ void scatter_copy_kernel_item(const ScatterArgs& a, int64_t t, int nth) {
+// Destination rows of the routed and replayed scatters: the routing lookup
+// (which also writes tok_map and packed_src) or the cached tok_map.
+template <int DMAX, bool REPLAY>
+struct LookupRows {
+    const ScatterArgs& a;
+    bool meta = true;   // this workgroup writes the token's tok_map / packed_src
+    __device__ __forceinline__ void operator()(int64_t t, int (&rows)[DMAX]) const {
+        token_rows<DMAX, REPLAY>(a, t, rows, meta);
+    }
+};
+
+// get_rows(t, rows) runs after the first loads of the row are issued, so
+// their latency overlaps it.
+template <int DMAX, int VPT, bool SC, class RowsFn>
+__device__ __forceinline__ void scatter_copy_item(const ScatterArgs& a, int64_t t, int nth,
+                                                  const RowsFn& get_rows) {
     const int tid = threadIdx.x;
     const int64_t row_bytes = a.H * a.x_bytes;
     const int nvec = (int)(row_bytes / 16);
@@ -83,7 +98,7 @@ __device__ __forceinline__ void scatter_copy_kernel_item(const ScatterArgs& a, i
     load_first_pass<VPT>(src, nvec, val, tid, nth);
 
     int rows[DMAX];
-    token_rows<DMAX, REPLAY>(a, t, rows);
+    get_rows(t, rows);
     // scales first: loading them after the row stores would reuse registers the
     // stores still read, and the compiler would wait for every store first
     if (SC) forward_scales<DMAX>(a, t, rows, nth);
@@ -93,15 +108,20 @@ __device__ __forceinline__ void scatter_copy_kernel_item(const ScatterArgs& a, i
                                                                    tid, nth);
 }
 
+template <int DMAX, int VPT, bool REPLAY, bool SC>
+__device__ __forceinline__ void scatter_copy_kernel_item(const ScatterArgs& a, int64_t t, int nth) {
+    scatter_copy_item<DMAX, VPT, SC>(a, t, nth, LookupRows<DMAX, REPLAY>{a});
+}
+
 // ---------------------------------------------------------------------------
 // plain dispatch, fused blockwise fp8 pack (bf16 in)
 // ---------------------------------------------------------------------------
 
 // Units [c*C, c*C + C) of token t's row (C a multiple of the 8 units of a
-// scale block); chunk 0 also writes the token's tok_map and packed_src.
-template <int DMAX, int UPT, bool REPLAY, bool FP4>
-__device__ __forceinline__ void scatter_fp8_kernel_item(const ScatterArgs& a, int64_t t, int nth,
-                                                        int c, int C) {
+// scale block); get_rows(t, rows) runs once the first loads are issued.
+template <int DMAX, int UPT, bool FP4, class RowsFn>
+__device__ __forceinline__ void scatter_fp8_item(const ScatterArgs& a, int64_t t, int nth, int c,
+                                                 int C, const RowsFn& get_rows) {
     const int tid = threadIdx.x;
     const int K = a.slot.K;
     const int64_t H = a.H;
@@ -125,7 +145,7 @@ __device__ __forceinline__ void scatter_fp8_kernel_item(const ScatterArgs& a, in
     }
 
     int rows[DMAX];
-    token_rows<DMAX, REPLAY>(a, t, rows, c == 0);
+    get_rows(t, rows);
     const int64_t prow = FP4 ? H / 2 : H;      // bytes per packed row
     for (int base = u0;;) {
         u32x4 q[UPT];
@@ -283,7 +303,9 @@ __global__ __launch_bounds__(kCopyThreads) void scatter_fp8_kernel(ScatterArgs a
     const int64_t items = a.T * nch;
     for (int64_t wi = blockIdx.x; wi < items; wi += gridDim.x) {
         const int64_t t = wi / nch;
-        scatter_fp8_kernel_item<DMAX, UPT, REPLAY, FP4>(a, t, nth, (int)(wi - t * nch), C);
+        const int c = (int)(wi - t * nch);
+        // chunk 0 writes the token's tok_map and packed_src
+        scatter_fp8_item<DMAX, UPT, FP4>(a, t, nth, c, C, LookupRows<DMAX, REPLAY>{a, c == 0});
     }
 }
 template <int DMAX, int VPT>
@@ -296,6 +318,116 @@ __global__ __launch_bounds__(kCopyThreads) void expand_kernel(ExpandArgs a, int 
     const int64_t total = a.recv_off[a.R];
     const int64_t n = total < a.recv_rows ? total : a.recv_rows;
     for (int64_t j = blockIdx.x; j < n; j += gridDim.x) expand_kernel_item<KMAX, VPT>(a, j, nth);
+}
+
+// ---------------------------------------------------------------------------
+// dispatch of one routing tile (T*K <= 1024 entries: decode-sized calls) in one
+// launch.  Every workgroup ranks the whole tile in its LDS (the rank pass of the
+// routing, 16 waves x one 64-entry chunk), scans the key totals there and so
+// knows every entry's row without waiting for any other workgroup; workgroup 0
+// also writes the routing outputs (packed_cnt, packed_off, stats) with the
+// routing's own scan.  Each workgroup then moves its token's row as the routed
+// scatter does.  Two launches (routing, then scatter) cost 13.2 us at T=32
+// H=6144 E=128 K=8, mostly in the routing's memory round trips and the kernel
+// boundary.
+// ---------------------------------------------------------------------------
+constexpr int kSmallThreads = kTile;   // one thread per entry of the tile
+
+enum class SmallMode { Copy, CopyScales, Fp8, Fp4 };
+
+// The rows of token t in a one-tile dispatch: the whole tile ranked in LDS, the
+// key totals scanned there (workgroup 0 also writes the routing outputs), then
+// the routing's entry rule with the tile's base 0.  Called by every thread of
+// the workgroup, after the token row's first loads are issued.
+template <int DMAX>
+struct SmallRows {
+    const ScatterArgs& a;
+    const ScanArgs& sc;
+    int nbits;
+    int32_t* run_all;     // LDS [16 waves][E]
+    int32_t* rank_lds;    // LDS [kTile]
+    int32_t* off_lds;     // LDS [E]
+    int32_t* flags_lds;   // LDS [2]
+    int32_t* wave_sums;   // LDS [16]
+    __device__ __forceinline__ void operator()(int64_t t, int (&rows)[DMAX]) const {
+        constexpr int kWaves = kSmallThreads / kWave;
+        const int tid = threadIdx.x;
+        const int lane = tid % kWave;
+        const int K = a.slot.K;
+        const int E = a.slot.E;
+        rank_tile<kWaves, 1>(ExpertKeys{a.slot.idx, E}, a.T * K, E, nbits, 0, run_all, rank_lds,
+                             nullptr, nullptr, flags_lds);
+        __syncthreads();
+        if (blockIdx.x == 0) {
+            const OneTileLds lds{run_all, kWaves, flags_lds};
+            scan_tiles_body<false>(sc, &lds);
+        }
+        int32_t tot = 0;
+        if (tid < E)
+            for (int w = 0; w < kWaves; ++w) tot += run_all[w * E + tid];
+        const int32_t excl = block_exclusive_scan(tot, wave_sums);
+        if (tid < E) off_lds[tid] = excl;
+        __syncthreads();
+        int my_row = -1;
+        if (lane < K) {
+            const int64_t f = t * K + lane;
+            const int32_t lr = rank_lds[f];
+            if (lr >= 0) {
+                const int32_t e = a.slot.idx[f];
+                const int64_t base = a.slot.cap > 0 ? (int64_t)e * a.slot.cap : (int64_t)off_lds[e];
+                const int64_t row = base + lr;
+                if (!((a.slot.cap > 0 && lr >= a.slot.cap) || row >= a.slot.packed_rows))
+                    my_row = (int)row;
+            }
+        }
+        if (tid < K) {
+            a.tok_map[t * K + tid] = my_row;
+            if (my_row >= 0) a.packed_src[my_row] = (int32_t)t;
+        }
+        broadcast_rows<DMAX>(my_row, rows);
+    }
+};
+
+// One workgroup per token (T <= 1024 here).
+template <int DMAX, SmallMode MODE>
+__global__ __launch_bounds__(kSmallThreads) void dispatch_small_kernel(ScatterArgs a, ScanArgs sc,
+                                                                       int nbits) {
+    extern __shared__ int32_t run_all[];            // [16 waves][E] running counts
+    __shared__ int32_t rank_lds[kTile];             // stable rank of each entry, -1: no key
+    __shared__ int32_t off_lds[kFusedMaxKeys];      // exclusive offsets of the keys
+    __shared__ int32_t flags_lds[2];
+    __shared__ int32_t wave_sums[kSmallThreads / kWave];
+    const int64_t t = blockIdx.x;
+    const SmallRows<DMAX> rows{a, sc, nbits, run_all, rank_lds, off_lds, flags_lds, wave_sums};
+    if constexpr (MODE == SmallMode::Copy)
+        scatter_copy_item<DMAX, 4, false>(a, t, kSmallThreads, rows);
+    else if constexpr (MODE == SmallMode::CopyScales)
+        scatter_copy_item<DMAX, 4, true>(a, t, kSmallThreads, rows);
+    else
+        scatter_fp8_item<DMAX, 2, MODE == SmallMode::Fp4>(a, t, kSmallThreads, 0, (int)(a.H / 16),
+                                                          rows);
+}
+
+template <SmallMode MODE>
+struct SmallLaunch {
+    template <int D, int V>
+    struct Launch {
+        static void go(dim3 g, int, const ScanArgs& sc, const ScatterArgs& a, int nbits,
+                       hipStream_t s) {
+            const size_t lds = sizeof(int32_t) * (size_t)(kSmallThreads / kWave) * a.slot.E;
+            dispatch_small_kernel<D, MODE><<<g, dim3(kSmallThreads), lds, s>>>(a, sc, nbits);
+        }
+    };
+};
+
+template <SmallMode MODE>
+hipError_t small_by_dmax(int D, dim3 grid, const ScanArgs& sc, const ScatterArgs& a, int nbits,
+                         hipStream_t s) {
+    if (D <= 2) SmallLaunch<MODE>::template Launch<2, 0>::go(grid, 0, sc, a, nbits, s);
+    else if (D <= 4) SmallLaunch<MODE>::template Launch<4, 0>::go(grid, 0, sc, a, nbits, s);
+    else if (D <= 8) SmallLaunch<MODE>::template Launch<8, 0>::go(grid, 0, sc, a, nbits, s);
+    else SmallLaunch<MODE>::template Launch<16, 0>::go(grid, 0, sc, a, nbits, s);
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -465,6 +597,23 @@ hipError_t launch_scatter(const ScatterArgs& a, hipStream_t s) {
                   : by_dmax<CopyMode<true, false>::Launch, 4>(a.slot.K, grid, th, a, s);
     return sc ? by_dmax<CopyMode<false, true>::Launch, 4>(a.slot.K, grid, th, a, s)
               : by_dmax<CopyMode<false, false>::Launch, 4>(a.slot.K, grid, th, a, s);
+}
+
+bool dispatch_small_fits(int64_t T, int K, int E) {
+    return T > 0 && T * K <= kTile && E <= kFusedMaxKeys;
+}
+
+hipError_t launch_dispatch_small(const ScatterArgs& a, const ScanArgs& sc, hipStream_t s) {
+    if (!dispatch_small_fits(a.T, a.slot.K, a.slot.E) || a.replay || sc.tiles != 1)
+        return hipErrorInvalidValue;
+    int nbits = 0;
+    while ((1 << nbits) < a.slot.E) ++nbits;
+    const dim3 grid((unsigned)a.T);
+    if (a.fp8)
+        return a.fp4 ? small_by_dmax<SmallMode::Fp4>(a.slot.K, grid, sc, a, nbits, s)
+                     : small_by_dmax<SmallMode::Fp8>(a.slot.K, grid, sc, a, nbits, s);
+    return a.x_scales ? small_by_dmax<SmallMode::CopyScales>(a.slot.K, grid, sc, a, nbits, s)
+                      : small_by_dmax<SmallMode::Copy>(a.slot.K, grid, sc, a, nbits, s);
 }
 
 hipError_t launch_recv_copy(const RecvArgs& a, hipStream_t s) {
