@@ -783,6 +783,46 @@ def test_fp4_end_to_end_skewed_full():
 
 
 # ---------------------------------------------------------------------------
+# one-launch dispatch of a single routing tile (T*K <= 1024, E <= 512) and its
+# boundary: the same ids just inside and just outside it give the oracle's
+# outputs either way
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,K,E", [(128, 8, 512), (128, 8, 513), (129, 8, 64), (1024, 1, 7)])
+@pytest.mark.parametrize("layout", ["compact", "padded_tight"])
+@pytest.mark.parametrize("payload", ["bf16", "f32", "fp8", "fp4", "prequant"])
+def test_dispatch_one_tile_boundary(T, K, E, layout, payload):
+    rng = np.random.default_rng(T + K + E)
+    idx = _mixed_idx(rng, T, K, E)
+    H = 256
+    flat = idx.ravel()
+    cnt = np.bincount(flat[(flat >= 0) & (flat < E)], minlength=E)
+    cap = 0 if layout == "compact" else max(1, int(cnt.max()) // 2)
+    rows = T * K if layout == "compact" else E * cap - 3
+    note(f"dispatch one-tile boundary {payload} {layout} T={T} K={K} E={E}")
+    if payload == "prequant":
+        q = rng.integers(0, 256, size=(T, H), dtype=np.uint8)
+        sc = (rng.random((T, H // 128)) + 0.5).astype(np.float32)
+        o = moe._lib.alloc_dispatch(T, H, K, E, rows, torch.uint8, True, DEV)
+        for t in (o.packed, o.scales, o.packed_src, o.tok_map, o.packed_cnt, o.packed_off, o.stats):
+            poison_(t)
+        moe.dispatch_prequant(dev(q), dev(sc), dev(idx), E, cap=cap, packed_rows=rows, out=o)
+        torch.cuda.synchronize()
+        ref = oracle.dispatch(q, "fp8", idx, E, cap=cap, packed_rows=rows, x_scales=sc)
+        assert_dispatch_equal(o, ref, fp8=True)
+        return
+    dt = "f32" if payload == "f32" else "bf16"
+    x = W.normal_x(rng, T, H, dt)
+    if payload in ("fp8", "fp4"):
+        x = W.inject_outliers(x, np.arange(0, T, 11), 1000.0)
+    o = gpu_dispatch(dev_x(x, dt), idx, E, cap=cap, packed_rows=rows, fp8=payload == "fp8",
+                     fp4=payload == "fp4")
+    ref = oracle.dispatch(x, dt, idx, E, cap=cap, packed_rows=rows,
+                          packed_dt=payload if payload in ("fp8", "fp4") else None)
+    assert_dispatch_equal(o, ref, fp8=payload in ("fp8", "fp4"))
+
+
+# ---------------------------------------------------------------------------
 # edge cases of the quantized and replay entry points
 # ---------------------------------------------------------------------------
 
