@@ -57,14 +57,15 @@ struct SurvivorKeys {
 // run_all: LDS of WAVES*NK ints.  All threads of the workgroup must call it.
 // flags_lds (optional, LDS): the workgroup scans its own tile (a one-tile
 // launch), so nothing is published: thread 0 leaves the two flag totals there
-// and the counts stay in run_all.
+// and the counts stay in run_all.  key_out (optional): each entry's key.
 template <int WAVES, int CHUNKS, class KeyFn>
 __device__ __forceinline__ void rank_tile(const KeyFn& keys, int64_t N, int NK, int nbits,
                                           int64_t tile, int32_t* run_all,
                                           int32_t* __restrict__ local_rank,
                                           int32_t* __restrict__ tile_cnt,
                                           int32_t* __restrict__ tile_flags,
-                                          int32_t* flags_lds = nullptr) {
+                                          int32_t* flags_lds = nullptr,
+                                          int32_t* key_out = nullptr) {
     static_assert(WAVES * CHUNKS * kWave == kTile, "tile size");
     __shared__ int32_t flag_cnt[WAVES][2];
     const int tid = threadIdx.x;
@@ -111,6 +112,7 @@ __device__ __forceinline__ void rank_tile(const KeyFn& keys, int64_t N, int NK, 
         if (key[c] >= 0)
             for (int w = 0; w < wave; ++w) r += run_all[w * NK + key[c]];
         local_rank[f] = r;
+        if (key_out) key_out[f] = key[c];
     }
     // The tile's counts and flags are read by another workgroup (the scan),
     // possibly in the same launch on another XCD: agent-scope stores write

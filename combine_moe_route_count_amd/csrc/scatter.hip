@@ -346,6 +346,7 @@ struct SmallRows {
     int nbits;
     int32_t* run_all;     // LDS [16 waves][E]
     int32_t* rank_lds;    // LDS [kTile]
+    int32_t* key_lds;     // LDS [kTile]: each entry's expert (valid where its rank is >= 0)
     int32_t* off_lds;     // LDS [E]
     int32_t* flags_lds;   // LDS [2]
     int32_t* wave_sums;   // LDS [16]
@@ -356,7 +357,7 @@ struct SmallRows {
         const int K = a.slot.K;
         const int E = a.slot.E;
         rank_tile<kWaves, 1>(ExpertKeys{a.slot.idx, E}, a.T * K, E, nbits, 0, run_all, rank_lds,
-                             nullptr, nullptr, flags_lds);
+                             nullptr, nullptr, flags_lds, key_lds);
         __syncthreads();
         if (blockIdx.x == 0) {
             const OneTileLds lds{run_all, kWaves, flags_lds};
@@ -373,7 +374,7 @@ struct SmallRows {
             const int64_t f = t * K + lane;
             const int32_t lr = rank_lds[f];
             if (lr >= 0) {
-                const int32_t e = a.slot.idx[f];
+                const int32_t e = key_lds[f];
                 const int64_t base = a.slot.cap > 0 ? (int64_t)e * a.slot.cap : (int64_t)off_lds[e];
                 const int64_t row = base + lr;
                 if (!((a.slot.cap > 0 && lr >= a.slot.cap) || row >= a.slot.packed_rows))
@@ -394,11 +395,13 @@ __global__ __launch_bounds__(kSmallThreads) void dispatch_small_kernel(ScatterAr
                                                                        int nbits) {
     extern __shared__ int32_t run_all[];            // [16 waves][E] running counts
     __shared__ int32_t rank_lds[kTile];             // stable rank of each entry, -1: no key
+    __shared__ int32_t key_lds[kTile];              // each entry's key
     __shared__ int32_t off_lds[kFusedMaxKeys];      // exclusive offsets of the keys
     __shared__ int32_t flags_lds[2];
     __shared__ int32_t wave_sums[kSmallThreads / kWave];
     const int64_t t = blockIdx.x;
-    const SmallRows<DMAX> rows{a, sc, nbits, run_all, rank_lds, off_lds, flags_lds, wave_sums};
+    const SmallRows<DMAX> rows{a,       sc,      nbits,     run_all,  rank_lds,
+                               key_lds, off_lds, flags_lds, wave_sums};
     if constexpr (MODE == SmallMode::Copy)
         scatter_copy_item<DMAX, 4, false>(a, t, kSmallThreads, rows);
     else if constexpr (MODE == SmallMode::CopyScales)

@@ -452,11 +452,12 @@ def test_routing_any_workspace_contents(fill):
         np.testing.assert_array_equal(host(st), rs)
 
 
-def test_dispatch_graph_replays():
+@pytest.mark.parametrize("T", [3000, 100])
+def test_dispatch_graph_replays(T):
     """A captured dispatch replays with the same launch arguments each time;
     every replay, with eager launches on the same workspace in between, must
-    give the eager result."""
-    T, K, E, H = 3000, 8, 64, 256
+    give the eager result.  T=100 (800 entries) is the one-launch dispatch."""
+    K, E, H = 8, 64, 256
     rng = np.random.default_rng(37)
     idx = _mixed_idx(rng, T, K, E)
     x = W.normal_x(rng, T, H, "bf16")
