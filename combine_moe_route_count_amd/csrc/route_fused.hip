@@ -55,8 +55,8 @@ __global__ __launch_bounds__(kFusedThreads) void route_fused_kernel(KeyFn keys, 
     __shared__ int32_t tile_flags_lds[2];
     const int tid = threadIdx.x;
     // A launch of one tile (up to 1024 entries: the decode-sized calls) is its
-    // own last workgroup: it scans its counts straight from LDS, with no wait
-    // for its stores, no ticket and no read back.
+    // own last workgroup: it keeps its counts in LDS and scans them there, so
+    // nothing is published, no ticket is taken and nothing is read back.
     const bool single = a.scan.tiles == 1;
     rank_tile<kFusedWaves, 1>(keys, a.N, a.scan.NK, a.nbits, (int64_t)blockIdx.x, run_all,
                               a.local_rank, a.scan.tile_cnt, (int32_t*)a.scan.tile_flags,

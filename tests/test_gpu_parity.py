@@ -352,6 +352,29 @@ def test_dedup_shapes(K, E, R, H):
         np.testing.assert_array_equal(host(ow), ew)
 
 
+@pytest.mark.parametrize("T", [1, 37, 128])
+def test_dedup_one_tile(T):
+    """Both routing levels of a small dedup dispatch fit one tile (T*R and T*K
+    at most 1024): the one-tile routing keeps its counts in LDS."""
+    K, E, R, H = 6, 64, 8, 256
+    rng = np.random.default_rng(T + 91)
+    idx = _mixed_idx(rng, T, K, E)
+    x = W.normal_x(rng, T, H, "f32")
+    w = rng.random((T, K)).astype(np.float32)
+    note(f"dedup one tile T={T}")
+    o = _gpu_dedup(dev(x), idx, E, R)
+    ref = oracle.dedup_dispatch(x, "f32", idx, E, R)
+    _assert_dedup_equal(o, ref)
+    rr = T * min(K, R)
+    plan = dict(R=R, idx=dev(idx), rank_slot=o.rank_slot, recv_rows=rr)
+    out, ow = moe.combine(o.packed, o.tok_map, dev(w), E=E, out_dtype=torch.float32, dedup=plan)
+    torch.cuda.synchronize()
+    eo, ew, _ = oracle.dedup_combine(ref["packed"], "f32", ref["tok_map"], w, idx, E, R,
+                                     ref["rank_slot"], rr, "f32")
+    _check_combine(host(out), eo, "f32")
+    np.testing.assert_array_equal(host(ow), ew)
+
+
 def test_dedup_workload_full():
     d = W.make_inputs("dedup")
     E, R, K, T, H = d["E"], d["R"], d["K"], d["T"], d["H"]
