@@ -596,6 +596,73 @@ def dedup_line(moe, W, args, dev, name="dedup"):
     return out
 
 
+def latency_configs(moe, W, dev, warmup=20, reps=50):
+    """Latency of the tiny, decode and prefill configurations (parity cases,
+    not bench lines): HIP events around each dispatch and combine, one buffer
+    set, a sleep kernel queued ahead of each pair so that host launch latency is
+    not timed; then the pair captured as one graph and replayed the same way.
+    Expert stand-in: identity (the packed rows are the combine's input)."""
+    import numpy as np
+    import torch
+
+    res = {}
+    for name in ("tiny", "decode", "prefill"):
+        d = W.make_inputs(name)
+        T, H, E, K = d["T"], d["H"], d["E"], d["K"]
+        cap = int(np.bincount(d["idx"].ravel(), minlength=E).max()) if d["layout"] == "padded" else 0
+        x = torch.from_numpy(d["x"].view(np.int16)).view(torch.bfloat16).to(dev)
+        idx = torch.from_numpy(d["idx"]).to(dev)
+        w = torch.from_numpy(d["w"]).to(dev)
+        ws = moe.workspace(T, K, E, 0, dev)
+        o = moe.dispatch(x, idx, E, cap=cap, ws=ws)
+        y = o.packed.clone()
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        ow = torch.empty(T, dtype=torch.float32, device=dev)
+
+        def pair():
+            moe.dispatch(x, idx, E, cap=cap, out=o, ws=ws)
+            moe.combine(y, o.tok_map, w, out=out, out_weights=ow)
+
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        disp, comb, both = [], [], []
+        for i in range(warmup + reps):
+            torch.cuda._sleep(2_000_000)
+            ev[0].record()
+            moe.dispatch(x, idx, E, cap=cap, out=o, ws=ws)
+            ev[1].record()
+            moe.combine(y, o.tok_map, w, out=out, out_weights=ow)
+            ev[2].record()
+            torch.cuda.synchronize()
+            if i >= warmup:
+                disp.append(ev[0].elapsed_time(ev[1]) * 1e3)
+                comb.append(ev[1].elapsed_time(ev[2]) * 1e3)
+                both.append(ev[0].elapsed_time(ev[2]) * 1e3)
+        cs = torch.cuda.Stream(dev)
+        cs.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(cs):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cs):
+                pair()
+        torch.cuda.synchronize()
+        graph = []
+        for i in range(warmup + reps):
+            torch.cuda._sleep(2_000_000)
+            ev[0].record()
+            g.replay()
+            ev[2].record()
+            torch.cuda.synchronize()
+            if i >= warmup:
+                graph.append(ev[0].elapsed_time(ev[2]) * 1e3)
+        med = lambda v: round(statistics.median(v), 2)
+        res[name] = {"T": T, "H": H, "E": E, "K": K, "cap": cap, "dispatch_us": med(disp),
+                     "combine_us": med(comb), "pair_us": med(both), "graph_pair_us": med(graph)}
+        log(f"[bench] {name}: dispatch {med(disp)} us, combine {med(comb)} us, pair {med(both)} us, "
+            f"graph pair {med(graph)} us")
+        del o, y, out, ow, g
+        torch.cuda.empty_cache()
+    return res
+
+
 def copy_ceiling(moe, dev, reps=10):
     """GB/s (bytes read + written) of the library's 16-byte streaming copy of
     1 GiB, on the same stream as the kernels."""
@@ -633,6 +700,8 @@ def main():
                     help="skip the line that feeds the fp8 rows straight to moe_combine_fp8")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-sample", type=int, default=1024)
+    ap.add_argument("--latency-configs", action="store_true",
+                    help="only time the tiny, decode and prefill configurations (one JSON line)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run the plain 1 GiB copy used to scale HBM counters")
     ap.add_argument("--profile-text", nargs=2, metavar=("PROF_DIR", "OUT_DIR"),
@@ -663,6 +732,9 @@ def main():
     torch.cuda.set_device(0)
     if args.calibrate_copy:
         calibrate_copy(args.steps)
+        return
+    if args.latency_configs:
+        print(json.dumps({"latency_configs": latency_configs(moe, W, dev)}), flush=True)
         return
     name = args.workload
     r = measure(moe, W, name, args, dev, graphs=not args.no_graph)
