@@ -151,9 +151,35 @@ def _short_kernel(name):
     import re
     name = re.sub(r"^void ", "", name)
     name = name.replace("moe::(anonymous namespace)::", "").replace("moe::", "")
+    name = re.sub(r"\((\w+)\)(\d+)", r"\1=\2", name)   # enum template arguments
     if not name.startswith("at::"):
         name = re.sub(r"\(.*$", "", name)
     return name[:90]
+
+
+LATENCY_PROFILE_RUN = ("rocprofv3 --kernel-trace --stats --output-format csv -d {d}/latency -o lat -- "
+                       "python bench.py --latency-configs")
+
+
+def latency_profile_text(prof_dir, out_dir):
+    """Text summary of the kernel trace of the --latency-configs run (tiny, decode
+    and prefill; eager then graph-replayed pairs)."""
+    import csv
+    cmd = LATENCY_PROFILE_RUN.format(d=prof_dir)
+    stats = list(csv.DictReader(open(os.path.join(prof_dir, "latency", "lat_kernel_stats.csv"))))
+    out = ["# Kernel trace: the tiny (T=64 H=256 E=8 K=2), decode (T=32 H=6144 E=128 K=8) and",
+           "# prefill (T=4096 H=7168 E=256 K=8, padded) configurations, MI355X",
+           f"# command: {cmd}",
+           "# (bench.py --latency-configs: per configuration 1 setup dispatch, 70 eager pairs and",
+           "#  70 graph replays, a 2e6-cycle sleep kernel ahead of each pair)",
+           f"# summary: python bench.py --latency-profile-text {prof_dir} profiles",
+           "# kernel | calls | avg us | min us | max us | % of GPU time", ""]
+    for r in stats:
+        out.append(f"{_short_kernel(r['Name']):70s} {int(r['Calls']):5d} "
+                   f"{float(r['AverageNs']) / 1e3:9.2f} {float(r['MinNs']) / 1e3:9.2f} "
+                   f"{float(r['MaxNs']) / 1e3:9.2f} {float(r['Percentage']):6.2f}")
+    with open(os.path.join(out_dir, "latency_configs_kernel_trace.txt"), "w") as fh:
+        fh.write("\n".join(out) + "\n")
 
 
 def profile_text(prof_dir, out_dir):
@@ -700,6 +726,8 @@ def main():
                     help="skip the line that feeds the fp8 rows straight to moe_combine_fp8")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-sample", type=int, default=1024)
+    ap.add_argument("--latency-profile-text", nargs=2, metavar=("PROF_DIR", "OUT_DIR"),
+                    help="write the text summary of the rocprofv3 run of --latency-configs")
     ap.add_argument("--latency-configs", action="store_true",
                     help="only time the tiny, decode and prefill configurations (one JSON line)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -715,6 +743,9 @@ def main():
         return
     if args.profile_text:
         profile_text(*args.profile_text)
+        return
+    if args.latency_profile_text:
+        latency_profile_text(*args.latency_profile_text)
         return
 
     if args.gpus != 1:
