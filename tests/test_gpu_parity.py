@@ -514,6 +514,52 @@ def test_dispatch_graph_replays(T):
         assert_dispatch_equal(other, ref, fp8=True)
 
 
+def test_two_streams_two_workspaces():
+    """The library keeps no state between calls: two streams, each with its own
+    workspace and buffers (one a one-launch dispatch, one multi-tile, one with
+    the fp8 pack), dispatch and combine concurrently, many times over; both
+    end with the oracle's results."""
+    cases = [(100, 8, 64, 256, False), (3000, 8, 256, 512, True)]
+    setups = []
+    for n, (T, K, E, H, fp8) in enumerate(cases):
+        rng = np.random.default_rng(500 + n)
+        idx = _mixed_idx(rng, T, K, E)
+        x = W.normal_x(rng, T, H, "bf16")
+        w = rng.random((T, K)).astype(np.float32)
+        if fp8:
+            x = W.inject_outliers(x, np.arange(0, T, 31), 1000.0)   # some scaled blocks
+        ref = oracle.dispatch(x, "bf16", idx, E, packed_dt="fp8" if fp8 else None)
+        if fp8:
+            eo, ew = oracle.combine_fp8(ref["packed"], ref["scales"], ref["tok_map"], w, "bf16")
+        else:
+            eo, ew = oracle.combine(ref["packed"], "bf16", ref["tok_map"], w, "bf16")
+        st = torch.cuda.Stream()
+        o = moe._lib.alloc_dispatch(T, H, K, E, T * K, torch.bfloat16, fp8, DEV)
+        for t in (o.packed, o.scales, o.packed_src, o.tok_map, o.packed_cnt, o.packed_off, o.stats):
+            poison_(t)   # rows past the counts are never written: they keep the poison
+        setups.append(dict(E=E, fp8=fp8, st=st, ws=moe.workspace(T, K, E), o=o, x=dev_bf16(x),
+                           idx=dev(idx), w=dev(w), ref=ref, eo=eo, ew=ew,
+                           out=torch.empty((T, H), dtype=torch.bfloat16, device=DEV),
+                           ow=torch.empty(T, dtype=torch.float32, device=DEV)))
+    torch.cuda.synchronize()
+    note("two streams, two workspaces")
+    for it in range(50):
+        for s_ in setups:
+            with torch.cuda.stream(s_["st"]):
+                moe.dispatch(s_["x"], s_["idx"], s_["E"], fp8=s_["fp8"], out=s_["o"], ws=s_["ws"])
+                if s_["fp8"]:
+                    moe.combine_fp8(s_["o"].packed, s_["o"].scales, s_["o"].tok_map, s_["w"],
+                                    out=s_["out"], out_weights=s_["ow"])
+                else:
+                    moe.combine(s_["o"].packed, s_["o"].tok_map, s_["w"], out=s_["out"],
+                                out_weights=s_["ow"])
+    torch.cuda.synchronize()
+    for s_ in setups:
+        assert_dispatch_equal(s_["o"], s_["ref"], fp8=s_["fp8"])
+        _check_combine(host(s_["out"]), s_["eo"], "bf16")
+        np.testing.assert_array_equal(host(s_["ow"]), s_["ew"])
+
+
 @pytest.mark.parametrize("nbytes", [0, 16, 4096 + 16, (1 << 20) + 48])
 def test_copy16_bytes(nbytes):
     """The copy-ceiling helper moves the bytes exactly (grid tail included)."""
