@@ -324,10 +324,11 @@ __global__ __launch_bounds__(kCopyThreads) void expand_kernel(ExpandArgs a, int 
 // dispatch of one routing tile (T*K <= 1024 entries: decode-sized calls) in one
 // launch.  Every workgroup ranks the whole tile in its LDS (the rank pass of the
 // routing, 16 waves x one 64-entry chunk), scans the key totals there and so
-// knows every entry's row without waiting for any other workgroup; workgroup 0
-// also writes the routing outputs (packed_cnt, packed_off, stats) with the
-// routing's own scan.  Each workgroup then moves its token's row as the routed
-// scatter does.  At T=32 H=6144 E=128 K=8 the dispatch takes 10.8 us this way
+// knows every entry's row without waiting for any other workgroup.  Workgroups
+// 0..T-1 then move their token's row as the routed scatter does; one more
+// workgroup writes the routing outputs (packed_cnt, packed_off, stats) with the
+// routing's own scan, off the token workgroups' path (done by the first token
+// workgroup, that scan made the launch 1.3 us longer at T=32 H=6144 K=8).  At T=32 H=6144 E=128 K=8 the dispatch takes 10.8 us this way
 // against 11.5 us as two launches (routing, then scatter), launch latency
 // included.
 // ---------------------------------------------------------------------------
@@ -336,13 +337,12 @@ constexpr int kSmallThreads = kTile;   // one thread per entry of the tile
 enum class SmallMode { Copy, CopyScales, Fp8, Fp4 };
 
 // The rows of token t in a one-tile dispatch: the whole tile ranked in LDS, the
-// key totals scanned there (workgroup 0 also writes the routing outputs), then
-// the routing's entry rule with the tile's base 0.  Called by every thread of
-// the workgroup, after the token row's first loads are issued.
+// key totals scanned there, then the routing's entry rule with the tile's base
+// 0.  Called by every thread of the workgroup, after the token row's first
+// loads are issued.
 template <int DMAX>
 struct SmallRows {
     const ScatterArgs& a;
-    const ScanArgs& sc;
     int nbits;
     int32_t* run_all;     // LDS [16 waves][E]
     int32_t* rank_lds;    // LDS [kTile]
@@ -359,10 +359,6 @@ struct SmallRows {
         rank_tile<kWaves, 1>(ExpertKeys{a.slot.idx, E}, a.T * K, E, nbits, 0, run_all, rank_lds,
                              nullptr, nullptr, flags_lds, key_lds);
         __syncthreads();
-        if (blockIdx.x == 0) {
-            const OneTileLds lds{run_all, kWaves, flags_lds};
-            scan_tiles_body<false>(sc, &lds);
-        }
         int32_t tot = 0;
         if (tid < E)
             for (int w = 0; w < kWaves; ++w) tot += run_all[w * E + tid];
@@ -389,7 +385,7 @@ struct SmallRows {
     }
 };
 
-// One workgroup per token (T <= 1024 here).
+// One workgroup per token (T <= 1024 here), then the routing outputs' workgroup.
 template <int DMAX, SmallMode MODE>
 __global__ __launch_bounds__(kSmallThreads) void dispatch_small_kernel(ScatterArgs a, ScanArgs sc,
                                                                        int nbits) {
@@ -400,8 +396,16 @@ __global__ __launch_bounds__(kSmallThreads) void dispatch_small_kernel(ScatterAr
     __shared__ int32_t flags_lds[2];
     __shared__ int32_t wave_sums[kSmallThreads / kWave];
     const int64_t t = blockIdx.x;
-    const SmallRows<DMAX> rows{a,       sc,      nbits,     run_all,  rank_lds,
-                               key_lds, off_lds, flags_lds, wave_sums};
+    if (t == a.T) {   // the routing outputs
+        constexpr int kWaves = kSmallThreads / kWave;
+        rank_tile<kWaves, 1>(ExpertKeys{a.slot.idx, a.slot.E}, a.T * a.slot.K, a.slot.E, nbits, 0,
+                             run_all, rank_lds, nullptr, nullptr, flags_lds);
+        __syncthreads();
+        const OneTileLds lds{run_all, kWaves, flags_lds};
+        scan_tiles_body<false>(sc, &lds);
+        return;
+    }
+    const SmallRows<DMAX> rows{a, nbits, run_all, rank_lds, key_lds, off_lds, flags_lds, wave_sums};
     if constexpr (MODE == SmallMode::Copy)
         scatter_copy_item<DMAX, 4, false>(a, t, kSmallThreads, rows);
     else if constexpr (MODE == SmallMode::CopyScales)
@@ -611,7 +615,7 @@ hipError_t launch_dispatch_small(const ScatterArgs& a, const ScanArgs& sc, hipSt
         return hipErrorInvalidValue;
     int nbits = 0;
     while ((1 << nbits) < a.slot.E) ++nbits;
-    const dim3 grid((unsigned)a.T);
+    const dim3 grid((unsigned)a.T + 1);   // the tokens, then the routing outputs
     if (a.fp8)
         return a.fp4 ? small_by_dmax<SmallMode::Fp4>(a.slot.K, grid, sc, a, nbits, s)
                      : small_by_dmax<SmallMode::Fp8>(a.slot.K, grid, sc, a, nbits, s);
