@@ -244,7 +244,8 @@ def combine_fp4(q: np.ndarray, scales, tok_map: np.ndarray, w: np.ndarray, out_d
 
 
 def e2m1_encode(v: np.ndarray) -> np.ndarray:
-    """Encode values to e2m1 codes (0..15), round to nearest even, saturating at 6."""
+    """Encode values to e2m1 codes (0..15), round to nearest even, saturating at 6
+    (infinities included); NaN gives code 0."""
     v = _c(v, np.float32)
     out = np.empty(v.shape, np.uint8)
     _load().oracle_e2m1_encode(_p(v), v.size, _p(out))
@@ -352,7 +353,8 @@ def bf16_encode(v: np.ndarray) -> np.ndarray:
 
 
 def e4m3_encode(v: np.ndarray) -> np.ndarray:
-    """Encode values with |v| <= 448 to OCP e4m3fn bytes (round to nearest even)."""
+    """Encode values to OCP e4m3fn bytes (round to nearest even; magnitudes above
+    448, infinities included, saturate to +-448; NaN gives S.1111.111)."""
     v = _c(v, np.float32)
     out = np.empty(v.shape, np.uint8)
     _load().oracle_e4m3_encode(_p(v), v.size, _p(out))

@@ -39,8 +39,18 @@
  *            the capacity, or past packed_rows, are dropped (tok_map = -1) and
  *            counted in stats[1]; the dropped ones are the latest in f.
  *   R-fp8    OCP e4m3fn (bias 7, max 448, no infinities), round to nearest even.
- *            Block of 128: amax = max|x|; amax > 448: s = amax/448 and
- *            q = e4m3(clamp((x*448)/amax)); otherwise s = 1 and q = e4m3(x).
+ *            Block of 128: amax = max|x| over the block's finite elements;
+ *            amax > 448: s = amax/448 and q = e4m3(x*448/amax), the quotient
+ *            of the exact product correctly rounded to f32 (no intermediate
+ *            overflow); otherwise s = 1 and q = e4m3(x).
+ *   R-nonfinite  the encoders saturate: +-inf (and any magnitude above the
+ *            format's maximum) give +-448 (e4m3) or +-6 (e2m1) with the sign
+ *            kept; NaN gives the e4m3 NaN code S.1111.111 with the NaN's sign.
+ *            e2m1 has no NaN code: a block holding a NaN is stored as all-zero
+ *            codes with a NaN block scale, so the whole block decodes to NaN
+ *            (the block-scale NaN convention of the OCP microscaling formats).
+ *            Infinities never count toward amax, so one infinity does not
+ *            flush its block to zero.
  *   R-comb   acc starts at +0.0f and takes, for k ascending, acc = acc + (w*y)
  *            with the product and the sum each rounded to f32 (no fused
  *            multiply-add).  out_weights[t] is the f32 sum of the weights of
@@ -50,7 +60,8 @@
  *            bf16 step, then the R-comb reduction over v.
  *   R-fp4    fp4 payload: OCP e2m1 (max 6), round to nearest even, two codes
  *            per byte with element 2i in the low nibble; the R-fp8 block rule
- *            with 6 in place of 448 (s = amax/6 when amax > 6, else 1).
+ *            with 6 in place of 448 (s = amax/6 when amax > 6, else 1), and
+ *            R-nonfinite.
  *   R-comb4  fp4 expert outputs: v = f32(e2m1(q)) * s, then the R-comb
  *            reduction, as R-comb8.
  *   R-prequant  fp8 input (e4m3 codes with one f32 scale per 128-element
@@ -73,8 +84,11 @@
  * bf16 encoder against torch's float32->bfloat16 rounding; combine against the
  * identity-expert closed form out = (sum_k w_k) * x, exact dyadic cases and
  * hand-derived order / fusion cases; dedup against python-set rank masks and
- * the plain dispatch of the same ids.  The choice of the fp8 scale rule among
- * the readings of the garbled formula is a reading, not a pin.
+ * the plain dispatch of the same ids; the non-finite and near-overflow
+ * handling of the block packs against hand-derived codes from the format
+ * definitions and against the power-of-two homogeneity of the block rule.
+ * The choice of the fp8 scale rule among the readings of the garbled formula
+ * is a reading, not a pin.
  *
  * Build: gcc -O2 -std=c99 -ffp-contract=off -fopenmp -shared -fPIC
  * (-ffp-contract=off keeps every multiply and add separately rounded).
@@ -128,11 +142,17 @@ static float e4m3_to_f32(uint8_t b) {
     return (float)((b & 0x80) ? -v : v);
 }
 
-/* Encode a value with |v| <= 448 to e4m3fn, round to nearest, ties to even.
- * The sign is kept for zero results (-0 and tiny negatives give 0x80). */
+/* Encode to e4m3fn, round to nearest, ties to even.  The sign is kept for
+ * zero results (-0 and tiny negatives give 0x80).  Saturating (R-nonfinite):
+ * a magnitude above 448, infinity included, gives +-448 (S.1111.110; between
+ * 448 and 464 that is also the nearest value); NaN gives S.1111.111. */
 static uint8_t f32_to_e4m3(float v) {
     uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    if (isnan(v))
+        return (uint8_t)(sign | 0x7F);
     double a = fabs((double)v);
+    if (a > 448.0)
+        return (uint8_t)(sign | 0x7E);
     if (a < 0.015625) {
         /* below 2^-6 the grid is the subnormal step 2^-9; a rounded count of 8
          * is exactly the smallest normal 2^-6, whose code is also 8 */
@@ -161,9 +181,13 @@ static float e2m1_to_f32(uint8_t n) {
 }
 
 /* Encode to e2m1, round to nearest, ties to the even code (mantissa bit 0);
- * magnitudes above 6 saturate to 6; the sign is kept for zero results. */
+ * magnitudes above 6, infinity included, saturate to 6; the sign is kept for
+ * zero results.  The format has no NaN: the block rule handles NaN before
+ * calling this, which maps it to code 0. */
 static uint8_t f32_to_e2m1(float v) {
     uint8_t sign = signbit(v) ? 8 : 0;
+    if (isnan(v))
+        return 0;
     double a = fabs((double)v);
     uint8_t best = 0;
     double bd = a;                              /* distance to code 0 */
@@ -188,67 +212,76 @@ static float load_elem(const void* base, int dt, int64_t i) {
 static size_t elem_bytes(int dt) { return dt == ORC_F32 ? 4 : (dt == ORC_BF16 ? 2 : 1); }
 
 /* ------------------------------------------------------------------ */
-/* fp8 blockwise pack of one row (reading R-fp8)                        */
+/* blockwise fp8 / fp4 pack of one row                                  */
 /* ------------------------------------------------------------------ */
 
 #define FP8_BLOCK 128
 #define E4M3_MAX 448.0f
 
+/* Largest magnitude among the finite elements of a 128-element bf16 block (0
+ * when none is finite); sets *has_nan when the block holds a NaN. */
+static float block_finite_amax(const uint16_t* xb, int* has_nan) {
+    float amax = 0.0f;
+    *has_nan = 0;
+    for (int h = 0; h < FP8_BLOCK; ++h) {
+        float x = bf16_to_f32(xb[h]);
+        if (isnan(x))
+            *has_nan = 1;
+        else if (isfinite(x) && fabsf(x) > amax)
+            amax = fabsf(x);
+    }
+    return amax;
+}
+
+/* x * m / amax for a bf16 x and a finite amax > m, rounded once to f32: the
+ * product is exact in double (8-bit and 3-bit significands, far inside the
+ * double range, so a block near the bf16 maximum does not overflow), the
+ * double quotient is correctly rounded, and rounding it on to f32 gives the
+ * correctly rounded f32 quotient because 53 >= 2*24 + 2 (double rounding is
+ * innocuous for division at that precision, S. A. Figueroa, "When is double
+ * rounding innocuous?", 1995).  Infinite x gives an infinite quotient and NaN
+ * stays NaN; the encoders saturate or keep them (R-nonfinite). */
+static float scaled_quotient(float x, float m, float amax) {
+    return (float)(((double)x * (double)m) / (double)amax);
+}
+
+/* fp8 blockwise pack of one row (readings R-fp8, R-nonfinite) */
 static void fp8_pack_row(const uint16_t* xrow, int64_t H, uint8_t* q, float* s) {
     for (int64_t b = 0; b * FP8_BLOCK < H; ++b) {
         const uint16_t* xb = xrow + b * FP8_BLOCK;
-        float amax = 0.0f;
+        int has_nan;
+        float amax = block_finite_amax(xb, &has_nan);
+        int scaled = amax > E4M3_MAX;
+        s[b] = scaled ? amax / E4M3_MAX : 1.0f;
         for (int h = 0; h < FP8_BLOCK; ++h) {
-            float a = fabsf(bf16_to_f32(xb[h]));
-            if (a > amax)
-                amax = a;
-        }
-        if (amax > E4M3_MAX) {
-            s[b] = amax / E4M3_MAX;
-            for (int h = 0; h < FP8_BLOCK; ++h) {
-                float v = bf16_to_f32(xb[h]) * E4M3_MAX; /* exact: 8-bit x 3-bit significands */
-                v = v / amax;
-                if (v > E4M3_MAX) v = E4M3_MAX;
-                if (v < -E4M3_MAX) v = -E4M3_MAX;
-                q[b * FP8_BLOCK + h] = f32_to_e4m3(v);
-            }
-        } else {
-            s[b] = 1.0f;
-            for (int h = 0; h < FP8_BLOCK; ++h)
-                q[b * FP8_BLOCK + h] = f32_to_e4m3(bf16_to_f32(xb[h]));
+            float v = bf16_to_f32(xb[h]);
+            if (scaled && !isnan(v))                  /* a NaN keeps its sign as it is */
+                v = scaled_quotient(v, E4M3_MAX, amax);   /* |v| <= 448 unless x is inf */
+            q[b * FP8_BLOCK + h] = f32_to_e4m3(v);
         }
     }
 }
 
-/* fp4 blockwise pack of one row (reading R-fp4): the R-fp8 rule with the e2m1
- * maximum 6.  Per 128-element block: amax = max|x|; amax > 6 gives s = amax/6
- * and q = e2m1(clamp((x*6)/amax, +-6)) (x*6 is exact for bf16 x); otherwise
- * s = 1 and q = e2m1(x).  Element 2i goes to the low nibble of byte i. */
+/* fp4 blockwise pack of one row (readings R-fp4, R-nonfinite): the R-fp8 rule
+ * with the e2m1 maximum 6.  Per 128-element block: amax over the finite
+ * elements; amax > 6 gives s = amax/6 and q = e2m1(x*6/amax); otherwise s = 1
+ * and q = e2m1(x).  A block holding a NaN gets s = NaN and all-zero codes.
+ * Element 2i goes to the low nibble of byte i. */
 #define E2M1_MAX 6.0f
 
 static void fp4_pack_row(const uint16_t* xrow, int64_t H, uint8_t* q, float* s) {
     for (int64_t b = 0; b * FP8_BLOCK < H; ++b) {
         const uint16_t* xb = xrow + b * FP8_BLOCK;
-        float amax = 0.0f;
-        for (int h = 0; h < FP8_BLOCK; ++h) {
-            float a = fabsf(bf16_to_f32(xb[h]));
-            if (a > amax)
-                amax = a;
-        }
+        int has_nan;
+        float amax = block_finite_amax(xb, &has_nan);
+        int scaled = amax > E2M1_MAX;
         uint8_t codes[FP8_BLOCK];
-        if (amax > E2M1_MAX) {
-            s[b] = amax / E2M1_MAX;
-            for (int h = 0; h < FP8_BLOCK; ++h) {
-                float v = bf16_to_f32(xb[h]) * E2M1_MAX;
-                v = v / amax;
-                if (v > E2M1_MAX) v = E2M1_MAX;
-                if (v < -E2M1_MAX) v = -E2M1_MAX;
-                codes[h] = f32_to_e2m1(v);
-            }
-        } else {
-            s[b] = 1.0f;
-            for (int h = 0; h < FP8_BLOCK; ++h)
-                codes[h] = f32_to_e2m1(bf16_to_f32(xb[h]));
+        s[b] = has_nan ? NAN : (scaled ? amax / E2M1_MAX : 1.0f);
+        for (int h = 0; h < FP8_BLOCK; ++h) {
+            float v = bf16_to_f32(xb[h]);
+            if (scaled)
+                v = scaled_quotient(v, E2M1_MAX, amax);
+            codes[h] = has_nan ? 0 : f32_to_e2m1(v);
         }
         for (int h = 0; h < FP8_BLOCK; h += 2)
             q[(b * FP8_BLOCK + h) / 2] = (uint8_t)(codes[h] | (codes[h + 1] << 4));

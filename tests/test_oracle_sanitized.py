@@ -1,6 +1,8 @@
 """The oracle built with AddressSanitizer and UndefinedBehaviorSanitizer
-(host code only) runs every entry point on small inputs, edge cases included,
-in a child process: no out-of-bounds access, no undefined arithmetic."""
+(float-cast-overflow included; host code only) runs every entry point on small
+inputs, edge cases and non-finite payloads included, in a child process: no
+out-of-bounds access, no undefined arithmetic, no out-of-range float-to-integer
+conversion."""
 import os
 import subprocess
 import sys
@@ -56,6 +58,23 @@ SCRIPT = textwrap.dedent("""
             oracle.dedup_dispatch(x, "bf16", idx, E, R, recv_rows=max(0, rr - 3))
     v = rng.standard_normal(4096).astype(np.float32) * 10
     oracle.e4m3_decode(oracle.e4m3_encode(v))
+    # non-finite and near-overflow payloads through every pack and combine
+    special = np.array([0x7F80, 0xFF80, 0x7FC0, 0xFFC1, 0x7F7F, 0xFF7F, 0x7F00, 0x0001, 0x8000],
+                       np.uint16)
+    xs = bf16(rng.standard_normal((6, 256)))
+    xs.reshape(-1)[rng.integers(0, xs.size, 40)] = rng.choice(special, 40)
+    xs[5, :128] = 0x7FC0
+    idx = rng.integers(0, 4, size=(6, 2)).astype(np.int32)
+    w = rng.random((6, 2)).astype(np.float32)
+    for pdt in ("fp8", "fp4"):
+        d = oracle.dispatch(xs, "bf16", idx, 4, packed_dt=pdt)
+        comb = oracle.combine_fp8 if pdt == "fp8" else oracle.combine_fp4
+        comb(d["packed"], d["scales"], d["tok_map"], w, "bf16")
+    q, s = oracle.fp8_pack_rows(xs)
+    oracle.combine(oracle.fp8_dequant(q, s), "bf16", np.arange(12).reshape(6, 2) % 6, w, "bf16")
+    oracle.e4m3_encode(np.float32([np.inf, -np.inf, np.nan, 3e38, -1e30]))
+    oracle.e2m1_encode(np.float32([np.inf, -np.inf, np.nan, 3e38, -1e30]))
+    oracle.bf16_encode(np.float32([np.inf, -np.inf, np.nan, 3.4e38]))
     oracle.e2m1_decode(oracle.e2m1_encode(np.clip(v, -6, 6)))
     oracle.fp4_pack_rows(bf16(rng.standard_normal((3, 256))))
     print("sanitized oracle: ok")
@@ -74,7 +93,8 @@ def test_oracle_under_asan_ubsan(tmp_path):
         pytest.skip("gcc sanitizer runtimes not installed")
     lib = tmp_path / "liboracle_san.so"
     subprocess.run(["gcc", "-O1", "-g", "-std=gnu99", "-ffp-contract=off", "-fno-fast-math",
-                    "-fopenmp", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+                    "-fopenmp", "-fsanitize=address,undefined,float-cast-overflow",
+                    "-fno-sanitize-recover=all",
                     "-fno-omit-frame-pointer", "-shared", "-fPIC", "-o", str(lib),
                     os.path.join(ROOT, "oracle", "moe_oracle.c"), "-lm"], check=True)
     env = dict(os.environ, MOE_ORACLE_LIB=str(lib), LD_PRELOAD=f"{asan}:{ubsan}",
