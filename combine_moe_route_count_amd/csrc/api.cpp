@@ -402,7 +402,8 @@ MOE_API int moe_combine(const void* y, moe_dtype y_dt, int64_t y_rows, int64_t H
     if (out_dt != MOE_BF16 && out_dt != MOE_F32)
         return fail(MOE_ERR_INVALID_ARG, "out dtype must be MOE_BF16 or MOE_F32");
     MOE_TRY(check_H(H, false));
-    if (y_rows < 0) return fail(MOE_ERR_INVALID_ARG, "y_rows must be >= 0");
+    if (y_rows < 0 || y_rows > kMaxRows)
+        return fail(MOE_ERR_INVALID_ARG, "y_rows must be in [0, 2^31-1]");
     MOE_TRY(check_rows_ptr(y, y_rows, "y"));
     MOE_TRY(check_rows_ptr(out, T, "out"));
     if (T > 0 && (!tok_map || !w)) return fail(MOE_ERR_INVALID_ARG, "tok_map and w must be non-NULL");
@@ -453,7 +454,8 @@ int combine_quant(const uint8_t* q, bool fp4, const float* scales, int64_t y_row
     if (out_dt != MOE_BF16 && out_dt != MOE_F32)
         return fail(MOE_ERR_INVALID_ARG, "out dtype must be MOE_BF16 or MOE_F32");
     MOE_TRY(check_H(H, true));
-    if (y_rows < 0) return fail(MOE_ERR_INVALID_ARG, "y_rows must be >= 0");
+    if (y_rows < 0 || y_rows > kMaxRows)
+        return fail(MOE_ERR_INVALID_ARG, "y_rows must be in [0, 2^31-1]");
     MOE_TRY(check_rows_ptr(q, y_rows, "q"));
     if (scales && !aligned(scales, 4)) return fail(MOE_ERR_INVALID_ARG, "scales is not 4-byte aligned");
     MOE_TRY(check_rows_ptr(out, T, "out"));

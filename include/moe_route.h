@@ -61,7 +61,7 @@
  * last error.
  *
  * Limits: 0 <= T, 1 <= K <= 16, 1 <= E <= 1024, T*K < 2^31, H > 0 with
- * H % 8 == 0 (H % 128 == 0 for fp8 and fp4), packed_rows and recv_rows <= 2^31-1,
+ * H % 8 == 0 (H % 128 == 0 for fp8 and fp4), packed_rows, recv_rows and y_rows <= 2^31-1,
  * row pointers 16-byte aligned, 1 <= R <= 32 with E % R == 0.
  */
 #ifndef MOE_ROUTE_H

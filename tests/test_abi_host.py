@@ -82,7 +82,8 @@ bad_plan = L.DedupPlan(3, 0x100000, 0x100000, 10, None)
 res["combine"] = {
     "K0": comb(K=0), "H7": comb(H=7), "y_fp8": comb(ydt=2), "out_fp8": comb(odt=2),
     "y_null": comb(y=None), "tm_null": comb(tm=None), "w_null": comb(w=None),
-    "out_unaligned": comb(out=A8), "y_rows_neg": comb(yr=-1),
+    "out_unaligned": comb(out=A8), "y_rows_neg": comb(yr=-1), "y_rows_huge": comb(yr=1 << 31),
+    "y_rows_2p32": comb(yr=1 << 32),
     "dd_R_not_divisor": comb(dd=ctypes.byref(bad_plan)),
 }
 
@@ -128,7 +129,8 @@ def c4(**kw):
                              a["out"], a["odt"], a["ow"], None)
     return [st, lib.moe_last_error().decode()]
 
-res["combine_fp4"] = {"H64": c4(H=64), "K0": c4(K=0), "out_fp4": c4(odt=3), "q_unaligned": c4(q=A8)}
+res["combine_fp4"] = {"H64": c4(H=64), "K0": c4(K=0), "out_fp4": c4(odt=3), "q_unaligned": c4(q=A8),
+                      "y_rows_huge": c4(yr=1 << 31)}
 res["dispatch"]["fp4_from_f32"] = disp(x_dt=1, pdt=3, scales=A, H=128)
 res["dispatch"]["fp4_no_scales"] = disp(pdt=3, H=128)
 res["dispatch"]["fp4_H64"] = disp(pdt=3, scales=A, H=64)
@@ -137,6 +139,7 @@ res["combine_fp8"] = {
     "H64": c8(H=64), "K0": c8(K=0), "K17": c8(K=17), "out_fp8": c8(odt=2), "q_null": c8(q=None),
     "q_unaligned": c8(q=A8), "scales_unaligned": c8(sc=P(0x100002)), "tm_null": c8(tm=None),
     "out_unaligned": c8(out=A8), "Tneg": c8(T=-1), "y_rows_neg": c8(yr=-1),
+    "y_rows_huge": c8(yr=1 << 31),
 }
 def rp(**kw):
     a = dict(x=A, xdt=0, xs=None, T=5, H=128, tm=A, K=2, rows=10, px=A, pdt=0, ps=None)
