@@ -67,11 +67,33 @@ __global__ __launch_bounds__(kFusedThreads) void route_fused_kernel(KeyFn keys, 
         scan_tiles_body<true>(a.scan, &lds);
         return;
     }
-    // Publication of the tile: its counts and flags were stored at agent scope
-    // (written through to the coherence point), so completing them is enough
-    // for the last workgroup to see them; an agent-scope release fence would
-    // also write back every dirty line of this XCD's L2, which the previous
-    // kernel's streaming stores fill, and measured about 10 us per launch.
+    // Publication of the tile, and why it needs no release / acquire pair.
+    // The LLVM AMDGPU memory model's code sequences for GFX942, which gfx950
+    // follows, implement agent scope as: monotonic store = global_store sc1,
+    // monotonic load = global_load sc1 (both reach the device coherence point
+    // past the XCD's own L2, which is not coherent with the other XCDs' L2s),
+    // release fence = buffer_wbl2 sc1 + s_waitcnt vmcnt(0), acquire fence =
+    // buffer_inv sc1.  Every value that crosses workgroups here is one of
+    // those monotonic accesses (the counts and flags stored in rank_tile, the
+    // loads in scan_tiles_body<true>, the ticket's atomics, which the compiler
+    // emits with no cache bypass because the device performs them at the
+    // coherence point).  The write-back half of a release exists for plain
+    // stores left dirty in L2, and none of the published data is such a store,
+    // so the part that matters is the wait: vmcnt(0) returns only once every
+    // sc1 store of this wave has been acknowledged by the coherence point, and
+    // the barrier after it holds the ticket until all 16 waves have waited.
+    // On the reading side, the invalidate half of an acquire exists for plain
+    // loads that could hit stale L2 lines; the scan reads with sc1 loads
+    // issued after its own ticket returned the last count (a control
+    // dependence through LDS and a barrier), and each earlier arrival followed
+    // its own acknowledged stores, so those loads see every count.  Formally
+    // monotonic accesses alone do not order data in the model; the ordering
+    // here is the hardware's completion order, which is what the model's
+    // release sequence itself relies on.  The regression guards are the GPU
+    // tests that run this kernel back to back on two streams, replayed from a
+    // graph and 10^4 times with changing sizes.  The fence measured about
+    // 10 us per launch: its write-back flushes every dirty line the previous
+    // kernel's streaming stores left in this XCD's L2.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (tid == 0) s_last = arrive_ticket(a.ticket) == (uint32_t)a.scan.tiles;
