@@ -72,9 +72,11 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                                           _P, _P, _P, _P, _P, _P, _SZ, _P]
     lib.moe_dispatch_replay.argtypes = [_P, _I32, _P, _I64, _I64, _P, _I32, _I64, _P, _I32, _P, _P]
     lib.moe_combine_fp4.argtypes = [_P, _P, _I64, _I64, _P, _P, _I64, _I32, _P, _I32, _P, _P]
+    lib.moe_dispatch_noalloc.argtypes = [_P, _I32, _I64, _I64, _P, _I32, _I32, _I64, _I64, _P,
+                                         _I32, _P, _P, _P, _P, _P, _P, _P]
     for fn in ("moe_route_count", "moe_dispatch", "moe_combine", "moe_dedup_dispatch",
                "moe_fp8_dequant", "moe_copy16", "moe_combine_fp8", "moe_dispatch_prequant",
-               "moe_dispatch_replay", "moe_combine_fp4"):
+               "moe_dispatch_replay", "moe_combine_fp4", "moe_dispatch_noalloc"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -183,6 +185,26 @@ def dispatch(x: torch.Tensor, idx: torch.Tensor, E: int, cap: int = 0,
                                packed_rows, ptr(o.packed), pdt, ptr(o.scales), ptr(o.packed_cnt),
                                ptr(o.packed_off), ptr(o.packed_src), ptr(o.tok_map), ptr(o.stats),
                                ptr(ws), ws.numel(), _stream(dev)))
+    return o
+
+
+def dispatch_noalloc(x: torch.Tensor, idx: torch.Tensor, E: int, cap: int = 0,
+                     packed_rows: Optional[int] = None, fp8: bool = False,
+                     out: Optional[DispatchOut] = None, fp4: bool = False) -> DispatchOut:
+    """dispatch() through moe_dispatch_noalloc: no workspace argument; the
+    library's static per-GPU workspace is used (out must be given by callers
+    that cannot allocate)."""
+    T, H = x.shape
+    K = idx.shape[1]
+    if packed_rows is None:
+        packed_rows = E * cap if cap > 0 else T * K
+    dev = x.device
+    o = alloc_dispatch(T, H, K, E, packed_rows, x.dtype, fp8, dev, fp4) if out is None else out
+    pdt = MOE_FP4_E2M1 if fp4 else (MOE_FP8_E4M3 if fp8 else dtype_code(x.dtype))
+    _check(load().moe_dispatch_noalloc(ptr(x), dtype_code(x.dtype), T, H, ptr(idx), K, E, cap,
+                                       packed_rows, ptr(o.packed), pdt, ptr(o.scales),
+                                       ptr(o.packed_cnt), ptr(o.packed_off), ptr(o.packed_src),
+                                       ptr(o.tok_map), ptr(o.stats), _stream(dev)))
     return o
 
 

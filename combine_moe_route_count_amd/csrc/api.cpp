@@ -305,11 +305,11 @@ moe::ScatterArgs scatter_args(const void* x, moe_dtype x_dt, const float* x_scal
     return sa;
 }
 
-int dispatch_impl(const void* x, moe_dtype x_dt, const float* x_scales, int64_t T, int64_t H,
-                  const int32_t* idx, int K, int E, int64_t cap, int64_t packed_rows,
-                  void* packed_x, moe_dtype packed_dt, float* packed_scales, int32_t* packed_cnt,
-                  int32_t* packed_off, int32_t* packed_src, int64_t* tok_map, int32_t* stats,
-                  void* ws, size_t ws_bytes, void* stream) {
+// Every argument check of a routed dispatch except the workspace.
+int check_dispatch(const void* x, moe_dtype x_dt, const float* x_scales, int64_t T, int64_t H,
+                   const int32_t* idx, int K, int E, int64_t cap, int64_t packed_rows,
+                   const void* packed_x, moe_dtype packed_dt, const float* packed_scales,
+                   const int32_t* packed_cnt, const int32_t* packed_src, const int64_t* tok_map) {
     MOE_TRY(check_routing(T, K, E, idx));
     MOE_TRY(check_payload(x, x_dt, x_scales, T, H, packed_rows, packed_x, packed_dt,
                           packed_scales));
@@ -318,6 +318,16 @@ int dispatch_impl(const void* x, moe_dtype x_dt, const float* x_scales, int64_t 
     if (packed_rows > 0 && !packed_src) return fail(MOE_ERR_INVALID_ARG, "packed_src is NULL");
     if (T > 0 && !tok_map) return fail(MOE_ERR_INVALID_ARG, "tok_map is NULL");
     if (tok_map && !aligned(tok_map, 8)) return fail(MOE_ERR_INVALID_ARG, "tok_map is not 8-byte aligned");
+    return MOE_OK;
+}
+
+int dispatch_impl(const void* x, moe_dtype x_dt, const float* x_scales, int64_t T, int64_t H,
+                  const int32_t* idx, int K, int E, int64_t cap, int64_t packed_rows,
+                  void* packed_x, moe_dtype packed_dt, float* packed_scales, int32_t* packed_cnt,
+                  int32_t* packed_off, int32_t* packed_src, int64_t* tok_map, int32_t* stats,
+                  void* ws, size_t ws_bytes, void* stream) {
+    MOE_TRY(check_dispatch(x, x_dt, x_scales, T, H, idx, K, E, cap, packed_rows, packed_x,
+                           packed_dt, packed_scales, packed_cnt, packed_src, tok_map));
     const Layout L = layout(T, K, E, 0);
     MOE_TRY(check_ws(ws, ws_bytes, L.total));
     hipStream_t s = (hipStream_t)stream;
@@ -355,6 +365,30 @@ MOE_API int moe_dispatch(const void* x, moe_dtype x_dt, int64_t T, int64_t H, co
     return dispatch_impl(x, x_dt, nullptr, T, H, idx, K, E, cap, packed_rows, packed_x, packed_dt,
                          packed_scales, packed_cnt, packed_off, packed_src, tok_map, stats, ws,
                          ws_bytes, stream);
+}
+
+MOE_API int moe_dispatch_noalloc(const void* x, moe_dtype x_dt, int64_t T, int64_t H,
+                                 const int32_t* idx, int K, int E, int64_t cap, int64_t packed_rows,
+                                 void* packed_x, moe_dtype packed_dt, float* packed_scales,
+                                 int32_t* packed_cnt, int32_t* packed_off, int32_t* packed_src,
+                                 int64_t* tok_map, int32_t* stats, void* stream) {
+    if (x_dt == MOE_FP8_E4M3)
+        return fail(MOE_ERR_INVALID_ARG, "fp8 input carries scales: use moe_dispatch_prequant");
+    // every argument check runs before the workspace lookup (which may touch
+    // the device once) and before any launch
+    MOE_TRY(check_dispatch(x, x_dt, nullptr, T, H, idx, K, E, cap, packed_rows, packed_x,
+                           packed_dt, packed_scales, packed_cnt, packed_src, tok_map));
+    const size_t need = layout(T, K, E, 0).total;
+    if (need > moe::kScratchBytes)
+        return fail(MOE_ERR_WORKSPACE,
+                    "T=%lld K=%d E=%d needs a %zu-byte workspace, more than the %zu bytes of the "
+                    "static one: use moe_dispatch with a workspace",
+                    (long long)T, K, E, need, moe::kScratchBytes);
+    void* ws = nullptr;
+    MOE_HIP(moe::scratch_for_stream((hipStream_t)stream, &ws), "moe_dispatch_noalloc workspace");
+    return dispatch_impl(x, x_dt, nullptr, T, H, idx, K, E, cap, packed_rows, packed_x, packed_dt,
+                         packed_scales, packed_cnt, packed_off, packed_src, tok_map, stats, ws,
+                         moe::kScratchBytes, stream);
 }
 
 MOE_API int moe_dispatch_prequant(const uint8_t* x_q, const float* x_scales, int64_t T, int64_t H,

@@ -147,6 +147,12 @@ hipError_t launch_fp8_dequant(const uint8_t* q, const float* scales, int64_t row
                               void* y, hipStream_t s);
 hipError_t launch_copy16(const void* src, void* dst, int64_t bytes, hipStream_t s);
 
+// The static workspace of moe_dispatch_noalloc (scratch.hip): its size, and the
+// device address of the copy on the GPU that owns stream s (looked up once per
+// GPU, with that GPU current).
+constexpr size_t kScratchBytes = (size_t)4 << 20;
+hipError_t scratch_for_stream(hipStream_t s, void** out);
+
 // ---------------------------------------------------------------------------
 // combine
 // ---------------------------------------------------------------------------

@@ -130,10 +130,15 @@ int moe_route_count(const int32_t* idx, int64_t T, int K, int E, int32_t* cnt, i
  *                from MOE_BF16 (fp4: [packed_rows,H/2] bytes, two codes per byte,
  *                element 2i in the low nibble)
  *   packed_scales out f32 [packed_rows,H/128] iff packed_dt is fp8 or fp4, else NULL.
- *                Per block, with M = 448 (e4m3) or 6 (e2m1): amax = max|x|;
- *                amax > M gives s = amax/M and q = enc((x*M)/amax); otherwise
- *                s = 1 and q = enc(x); enc rounds to nearest even (the fp4 rule
- *                is the fp8 rule of the pages carried to the e2m1 maximum).
+ *                Per block, with M = 448 (e4m3) or 6 (e2m1): amax = max|x| over
+ *                the block's finite values; amax > M gives s = amax/M and
+ *                q = enc(x*M/amax), the correctly rounded f32 quotient (no
+ *                overflow of x*M); otherwise s = 1 and q = enc(x); enc rounds
+ *                to nearest even and saturates (+-inf give +-M, the clamp
+ *                before conversion of the pages' fp8 quantizer); a NaN gets the
+ *                e4m3 NaN code with its sign; e2m1 has no NaN code, so a block
+ *                holding a NaN gets zero codes and the NaN scale 0x7FC00000
+ *                (the fp4 rule is the fp8 rule carried to the e2m1 maximum).
  *   packed_cnt   out int32 [E]   rows written per expert
  *   packed_off   out int32 [E+1] first row of each expert's segment,
  *                min(e*cap or off[e], packed_rows); may be NULL
@@ -144,6 +149,24 @@ int moe_dispatch(const void* x, moe_dtype x_dt, int64_t T, int64_t H, const int3
                  float* packed_scales, int32_t* packed_cnt, int32_t* packed_off,
                  int32_t* packed_src, int64_t* tok_map, int32_t* stats, void* ws, size_t ws_bytes,
                  void* stream);
+
+/* moe_dispatch for callers that cannot allocate device memory (code under
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same arguments, results, checks and errors, without the workspace.  The
+ * routing workspace is a static device array of the library, 4 MiB on each
+ * GPU the library runs on, held from the first call on that GPU until the
+ * process ends; its device address is looked up once per GPU (that first call
+ * may briefly make the stream's GPU current).  The call allocates nothing.
+ * Limit: moe_workspace_size(T, K, E, 0) <= 4 MiB (T*K up to 837120 entries at
+ * E = 256, 523136 at E = 1024); larger sizes return MOE_ERR_WORKSPACE before
+ * anything is enqueued.  Every moe_dispatch_noalloc call on one GPU shares the
+ * array: calls that may overlap (different streams) race and must be ordered
+ * by the caller; calls on one stream are ordered by it. */
+int moe_dispatch_noalloc(const void* x, moe_dtype x_dt, int64_t T, int64_t H, const int32_t* idx,
+                         int K, int E, int64_t cap, int64_t packed_rows, void* packed_x,
+                         moe_dtype packed_dt, float* packed_scales, int32_t* packed_cnt,
+                         int32_t* packed_off, int32_t* packed_src, int64_t* tok_map,
+                         int32_t* stats, void* stream);
 
 /* Dispatch of pre-quantized input (the dispatch of "Draft: cco + flydsl
  * dispatch/combine", commit "... routing handle, LEC, reset, replay", forwards

@@ -168,6 +168,22 @@ res["prequant"] = {
     "ws_small": pq(wsb=ws_need - 1), "idx_null": pq(idx=None), "xs_unaligned": pq(xs=P(0x100002)),
 }
 res["dispatch"]["fp8_input"] = disp(x_dt=2, pdt=2, scales=A, H=128)
+
+def na(**kw):
+    a = dict(x=A, x_dt=0, T=100, H=64, idx=A, K=4, E=16, cap=0, rows=400, packed=A, pdt=0,
+             scales=None, pc=A, po=None, ps=A, tm=A, st=None)
+    a.update(kw)
+    st = lib.moe_dispatch_noalloc(a["x"], a["x_dt"], a["T"], a["H"], a["idx"], a["K"], a["E"],
+                                  a["cap"], a["rows"], a["packed"], a["pdt"], a["scales"], a["pc"],
+                                  a["po"], a["ps"], a["tm"], a["st"], None)
+    return [st, lib.moe_last_error().decode()]
+
+res["noalloc"] = {
+    "too_big_E256": na(T=104641, K=8, E=256, rows=837128), "too_big_E1024": na(T=65536, K=8, E=1024),
+    "K0": na(K=0), "E1025": na(E=1025), "H12": na(H=12), "x_null": na(x=None),
+    "fp8_input": na(x_dt=2, pdt=2, scales=A, H=128), "pc_null": na(pc=None),
+    "tok_map_unaligned": na(tm=A4), "fp8_no_scales": na(pdt=2, H=128),
+}
 res["route"] = {
     "cnt_null": [lib.moe_route_count(A, 10, 2, 4, None, A, None, WS, 1 << 20, None),
                  lib.moe_last_error().decode()],
@@ -251,3 +267,12 @@ def test_dedup_and_helpers_argument_errors():
         assert st == INVALID and msg, (case, st, msg)
     r = _res()["route"]
     assert r["cnt_null"][0] == INVALID and r["ws_small"][0] == WORKSPACE
+
+
+def test_noalloc_dispatch_argument_errors():
+    """The static-workspace dispatch rejects sizes past its 4 MiB array and bad
+    arguments on the host, before it looks anything up on a device."""
+    for case, (st, msg) in _res()["noalloc"].items():
+        want = WORKSPACE if case.startswith("too_big") else INVALID
+        assert st == want and msg, (case, st, msg)
+    assert "static" in _res()["noalloc"]["too_big_E256"][1]

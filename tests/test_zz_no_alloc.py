@@ -1,0 +1,82 @@
+"""moe_dispatch_noalloc (the routing workspace is the library's static per-GPU
+array) against moe_dispatch (the caller's workspace) through the C ABI: every
+output bitwise equal, on two calls in a row with the second one smaller, for
+each payload, for the one-launch and the two-launch routing, and at the
+largest size the static workspace holds."""
+import numpy as np
+import pytest
+import torch
+
+import combine_moe_route_count_amd as moe
+import workloads as W
+from _gpu_util import DEV, dev, dev_bf16, host, note, poison_
+
+pytestmark = pytest.mark.gpu
+
+
+def _idx(rng, T, K, E):
+    idx = rng.integers(0, E, size=(T, K)).astype(np.int32)
+    idx[rng.random((T, K)) < 0.03] = -1
+    return idx
+
+
+def _both(x, idx_np, E, cap, rows, fp8, fp4):
+    T, H = x.shape
+    K = idx_np.shape[1]
+    outs = []
+    for fn in ("dispatch", "dispatch_noalloc"):
+        o = moe._lib.alloc_dispatch(T, H, K, E, rows, x.dtype, fp8, DEV, fp4=fp4)
+        for t in (o.packed, o.scales, o.packed_src, o.tok_map, o.packed_cnt, o.packed_off,
+                  o.stats):
+            poison_(t)
+        getattr(moe, fn)(x, dev(idx_np), E, cap=cap, packed_rows=rows, fp8=fp8, fp4=fp4, out=o)
+        outs.append(o)
+    torch.cuda.synchronize()
+    a, b = outs
+    for name in ("tok_map", "packed_cnt", "packed_off", "packed_src", "stats", "packed"):
+        ga, gb = host(getattr(a, name)), host(getattr(b, name))
+        assert np.array_equal(ga.view(np.uint8), gb.view(np.uint8)), name
+    if a.scales is not None:
+        assert np.array_equal(host(a.scales).view(np.uint32), host(b.scales).view(np.uint32))
+    return a
+
+
+# (payload, first T, second T, K, E, H, layout): the second call is smaller; T*K
+# <= 1024 takes the one-launch dispatch, larger sizes the two-launch routing
+CASES = [
+    ("bf16", 3000, 1100, 8, 256, 512, "compact"),
+    ("bf16", 2000, 40, 4, 64, 256, "padded"),
+    ("f32", 1500, 700, 6, 32, 128, "compact"),
+    ("fp8", 2500, 300, 8, 256, 1024, "compact"),
+    ("fp8", 900, 100, 8, 128, 7168, "padded"),
+    ("fp4", 2100, 257, 8, 256, 512, "compact"),
+]
+
+
+@pytest.mark.parametrize("payload,T1,T2,K,E,H,layout", CASES)
+def test_noalloc_equals_dispatch_twice(payload, T1, T2, K, E, H, layout):
+    rng = np.random.default_rng(T1 + T2 + K + H)
+    for T in (T1, T2):
+        idx = _idx(rng, T, K, E)
+        dt = "f32" if payload == "f32" else "bf16"
+        xs = W.normal_x(rng, T, H, dt)
+        x = dev(xs.astype(np.float32)) if dt == "f32" else dev_bf16(xs)
+        flat = idx.ravel()
+        cnt = np.bincount(flat[flat >= 0], minlength=E)
+        cap = int(cnt.max()) if layout == "padded" else 0
+        rows = E * cap if cap else T * K
+        note(f"noalloc {payload} T={T} K={K} E={E} H={H} {layout}")
+        _both(x, idx, E, cap, rows, payload == "fp8", payload == "fp4")
+
+
+def test_noalloc_at_the_static_workspace_limit():
+    """T*K = 837120 entries at E = 256: the largest routing the 4 MiB array
+    holds; then a small call again."""
+    rng = np.random.default_rng(5)
+    for T, K, E, H in [(104640, 8, 256, 64), (33, 8, 256, 64)]:
+        assert moe.workspace_size(T, K, E) <= 4 << 20
+        idx = _idx(rng, T, K, E)
+        x = dev_bf16(W.normal_x(rng, T, H, "bf16"))
+        note(f"noalloc limit T={T} K={K} E={E} H={H}")
+        _both(x, idx, E, 0, T * K, False, False)
+    assert moe.workspace_size(104641, 8, 256) > 4 << 20
