@@ -67,17 +67,18 @@ COMBINE_SOURCES = ["combine_moe_route_count_amd/csrc/combine.hip",
                    "combine_moe_route_count_amd/csrc/device_common.hpp"]
 
 
-def stored_traffic(kernel_hash):
-    """HBM bytes per combine launch from the committed rocprofv3 counter summary,
-    or None when it is missing or was taken on a different kernel source."""
+def stored_profile(kernel_hash):
+    """The committed rocprofv3 summary of the combine kernel (HBM bytes per launch
+    from the counters, average duration from the kernel trace), or {} when it is
+    missing or was taken on a different kernel source."""
     path = os.path.join(ROOT, "profiles", "combine_skewed_fp8_pmc.json")
     if not os.path.exists(path):
-        return None
+        return {}
     with open(path) as f:
         d = json.load(f)
     if d.get("combine_source_hash") != kernel_hash:
-        return None
-    return d.get("traffic_bytes_per_launch")
+        return {}
+    return d
 
 
 COPY_BYTES = 1 << 30   # calibration copy: 1 GiB read + 1 GiB written per launch
@@ -97,20 +98,25 @@ def calibrate_copy(steps):
     log(f"[bench] calibration copy of {COPY_BYTES} bytes x {steps} done")
 
 
-def _pmc_rows(path, kernel_substr):
+# The headline combine (bf16 y, bf16 out, K <= 8) as its name starts in the trace.
+HEADLINE_COMBINE = "combine_kernel<false, false, 8>"
+
+
+def _pmc_rows(path, kernel_prefix):
     import csv
     vals = []
     for r in csv.DictReader(open(path)):
-        if kernel_substr in r["Kernel_Name"]:
+        if _short_kernel(r["Kernel_Name"]).startswith(kernel_prefix):
             vals.append(float(r["Counter_Value"]))
     return vals
 
 
-def pmc_summary(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, out_json):
-    """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the combine kernel,
-    scaled by what the same counters read for the 1 GiB calibration copy."""
-    f = _pmc_rows(fetch_csv, "combine_kernel")
-    wv = _pmc_rows(write_csv, "combine_kernel")
+def pmc_summary(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, out_json, trace_avg_us=None):
+    """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the headline combine
+    kernel, scaled by what the same counters read for the 1 GiB calibration
+    copy; with the kernel trace's average duration of that kernel when given."""
+    f = _pmc_rows(fetch_csv, HEADLINE_COMBINE)
+    wv = _pmc_rows(write_csv, HEADLINE_COMBINE)
     cf = _pmc_rows(cal_fetch_csv, "copy16_kernel")
     cw = _pmc_rows(cal_write_csv, "copy16_kernel")
     cf_avg = statistics.mean(x for x in cf if x > 0)
@@ -125,26 +131,37 @@ def pmc_summary(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, out_json):
          "write_bytes_per_unit": write_scale,
          "fetch_bytes_per_launch": f_avg * fetch_scale, "write_bytes_per_launch": w_avg * write_scale,
          "traffic_bytes_per_launch": f_avg * fetch_scale + w_avg * write_scale,
+         "trace_avg_us": trace_avg_us,
          "combine_source_hash": source_hash(COMBINE_SOURCES)}
     with open(out_json, "w") as fh:
         json.dump(d, fh, indent=1)
     print(json.dumps(d, indent=1))
 
 
+# rocprofv3 runs behind the committed summaries under profiles/ (run with -d DIR,
+# then `python bench.py --profile-text DIR profiles`).  The kernel trace covers a
+# default bench run without the CPU leg; the counter runs, one per workload so
+# that kernels shared by several workloads are not mixed, read FETCH_SIZE and
+# WRITE_SIZE in runs of their own, and the library's 1 GiB copy calibrates them.
+PROFILE_WORKLOADS = {
+    "skewed_fp8": "--steps 5 --warmup 2 --no-cpu --no-graph --no-latency --secondary none --no-dedup",
+    "uniform_bf16": "--workload uniform_bf16 --steps 5 --warmup 2 --no-cpu --no-graph --no-latency "
+                    "--secondary none --no-dedup",
+    "dedup": "--only-dedup --steps 5 --warmup 2",
+    "prefill": "--latency-configs --latency-names prefill --latency-reps 5",
+}
 PROFILE_RUNS = {
     "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d {d}/trace -o bench -- "
-             "python bench.py --steps 10 --warmup 5 --no-cpu --secondary none",
-    "FETCH_SIZE": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/FETCH_SIZE -o bench -- "
-                  "python bench.py --steps 5 --warmup 2 --no-cpu --no-graph --secondary none "
-                  "--no-fp8-combine --no-dedup",
-    "WRITE_SIZE": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/WRITE_SIZE -o bench -- "
-                  "python bench.py --steps 5 --warmup 2 --no-cpu --no-graph --secondary none "
-                  "--no-fp8-combine --no-dedup",
+             "python bench.py --steps 10 --warmup 5 --no-cpu --no-latency",
     "cal_FETCH_SIZE": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/cal_FETCH_SIZE -o copy -- "
                       "python bench.py --calibrate-copy --steps 3",
     "cal_WRITE_SIZE": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/cal_WRITE_SIZE -o copy -- "
                       "python bench.py --calibrate-copy --steps 3",
 }
+for _w, _a in PROFILE_WORKLOADS.items():
+    for _c in ("FETCH_SIZE", "WRITE_SIZE"):
+        PROFILE_RUNS[f"{_w}_{_c}"] = (f"rocprofv3 --pmc {_c} --output-format csv -d {{d}}/{_w}_{_c} "
+                                      f"-o bench -- python bench.py {_a}")
 
 
 def _short_kernel(name):
@@ -182,22 +199,67 @@ def latency_profile_text(prof_dir, out_dir):
         fh.write("\n".join(out) + "\n")
 
 
+def dedup_rows(W):
+    """Recv rows (distinct (token, rank) pairs) and packed rows of the dedup
+    workload, from its routing alone."""
+    import numpy as np
+    d = W.make_inputs("dedup")
+    er = d["E"] // d["R"]
+    idx = d["idx"]
+    valid = (idx >= 0) & (idx < d["E"])
+    ranks = np.where(valid, idx // er, -1)
+    n_recv = sum(len(set(r[r >= 0].tolist())) for r in ranks)
+    return d, n_recv, int(valid.sum())
+
+
+def kernel_algorithmic_bytes(W):
+    """Algorithmic bytes per launch (or per call, for groups of kernels) of the
+    kernels the counter summaries compare against, by workload."""
+    out = {}
+    db, cb = algorithmic_bytes(8192, 7168, 8, 256, 8192 * 8, fp8=True)
+    out["skewed_fp8"] = {("route_fused_kernel<ExpertKeys>", "scatter_fp8_kernel<8, 2, false, false>"): db,
+                         (HEADLINE_COMBINE,): cb}
+    db, cb = algorithmic_bytes(8192, 7168, 8, 256, 8192 * 8, fp8=False)
+    out["uniform_bf16"] = {("route_fused_kernel<ExpertKeys>", "scatter_copy_kernel<8, 4, false, false>"): db,
+                           (HEADLINE_COMBINE,): cb}
+    db, cb = algorithmic_bytes(4096, 7168, 8, 256, 4096 * 8, fp8=False)
+    out["prefill"] = {("route_fused_kernel<ExpertKeys>", "scatter_copy_kernel<8, 4, false, false>"): db,
+                      (HEADLINE_COMBINE,): cb}
+    d, n_recv, n_rows = dedup_rows(W)
+    T, H, K, R = d["T"], d["H"], d["K"], d["R"]
+    row = H * 4
+    meta_d = T * K * 4 + T * K * 8 + n_rows * 4 + n_recv * 4 + T * R * 4
+    comb_fused = n_rows * row + T * row + T * K * 16 + T * R * 4 + T * 4
+    out["dedup"] = {("route_fused_kernel<RankKeys>", "recv_copy_kernel<8, 4>",
+                     "route_fused_kernel<SurvivorKeys>", "expand_kernel<8, 4>"):
+                    T * row + 2 * n_recv * row + n_rows * row + meta_d,
+                    ("recv_copy_kernel<8, 4>",): T * row + n_recv * row,
+                    ("expand_kernel<8, 4>",): n_recv * row + n_rows * row,
+                    ("dedup_combine_kernel<true, true, 6, 0>",): comb_fused,
+                    ("dedup_combine_kernel<true, true, 6, 1>", "dedup_sum_kernel<true, 6>"):
+                    comb_fused + 2 * n_recv * row}
+    return out
+
+
 def profile_text(prof_dir, out_dir):
     """Text summaries of the rocprofv3 runs in PROFILE_RUNS (run with -d prof_dir):
-    per-kernel trace statistics, HBM bytes per dispatch from FETCH_SIZE / WRITE_SIZE
-    scaled by the 1 GiB calibration copy, and the combine's counter JSON."""
+    per-kernel trace statistics, HBM bytes per dispatch from FETCH_SIZE /
+    WRITE_SIZE scaled by the 1 GiB calibration copy (per workload, against the
+    algorithmic bytes), and the headline combine's counter / trace JSON."""
     import collections
     import csv
+    import workloads as W
     cmd = {k: v.format(d=prof_dir) for k, v in PROFILE_RUNS.items()}
-    work = "skewed_fp8 workload (T=8192 H=7168 E=256 K=8, Zipf 1.2, fp8 payload), MI355X"
     stats = list(csv.DictReader(open(os.path.join(prof_dir, "trace", "bench_kernel_stats.csv"))))
     avg_us = {}
-    out = [f"# Kernel trace: {work}", f"# command: {cmd['trace']}",
-           "# (bench.py: the headline pair (3 setup dispatches + dequants, 5 warmup, 2x10 timed,",
-           "#  3 + 5 + 10 graph-replayed pairs and as many split dispatch / combine replays), the",
-           "#  fp8-input combine pair, the fp4 payload pair, the dispatch variants (replay,",
-           "#  pre-quantized), the dedup workload line (T=16384 H=4096 E=64 K=6 R=8 f32) and the",
-           "#  1 GiB 16-byte copy ceiling: 3 warmup + 10 timed copies)",
+    out = ["# Kernel trace of a default bench.py run without the CPU leg, MI355X:",
+           "#  the headline skewed_fp8 pair (T=8192 H=7168 E=256 K=8, Zipf 1.2, fp8 payload):",
+           "#  3 setup dispatches + dequants, 5 warmup, 2x10 timed, 3 + 5 + 10 graph-replayed pairs",
+           "#  and as many split dispatch / combine replays; the uniform_bf16 line (same shape,",
+           "#  uniform routing, bf16 payload) the same way; the fp8-input combine pair, the fp4",
+           "#  payload pair, the dispatch variants (replay, pre-quantized); the dedup line",
+           "#  (T=16384 H=4096 E=64 K=6 R=8 f32); the 1 GiB 16-byte copy ceiling",
+           f"# command: {cmd['trace']}",
            f"# summary: python bench.py --profile-text {prof_dir} profiles",
            "# kernel | calls | avg us | min us | max us | % of GPU time", ""]
     for r in stats:
@@ -215,95 +277,160 @@ def profile_text(prof_dir, out_dir):
             d[_short_kernel(r["Kernel_Name"])].append(float(r["Counter_Value"]))
         return d
 
-    fetch = per_kernel("FETCH_SIZE", "bench_counter_collection.csv")
-    write = per_kernel("WRITE_SIZE", "bench_counter_collection.csv")
     cf = statistics.mean(x for x in per_kernel("cal_FETCH_SIZE", "copy_counter_collection.csv")
                          ["copy16_kernel"] if x > 0)
     cw = statistics.mean(x for x in per_kernel("cal_WRITE_SIZE", "copy_counter_collection.csv")
                          ["copy16_kernel"] if x > 0)
     fs, wsc = COPY_BYTES / cf, COPY_BYTES / cw
-    lines = [f"# HBM traffic per dispatch from rocprofv3 counters: {work}", "# commands:"]
-    lines += [f"#   {cmd[k]}" for k in ("FETCH_SIZE", "WRITE_SIZE", "cal_FETCH_SIZE", "cal_WRITE_SIZE")]
+    alg = kernel_algorithmic_bytes(W)
+    lines = ["# HBM traffic per kernel dispatch from rocprofv3 counters, MI355X, one counter run per",
+             "# workload and counter (kernels shared by several workloads are not mixed)", "# commands:"]
+    lines += [f"#   {cmd[k]}" for k in PROFILE_RUNS if k != "trace"]
     lines += [f"#   python bench.py --profile-text {prof_dir} profiles",
               f"# calibration: the library's 16-byte copy of 1 GiB reads FETCH_SIZE {cf:.0f} and "
               f"WRITE_SIZE {cw:.0f};",
               f"#   bytes per counter unit: fetch {fs:.1f}, write {wsc:.1f}",
-              "# kernel | dispatches | fetch MB | write MB (averages per dispatch, scaled) | "
-              "GB/s over the trace's average duration", ""]
-    tot = {}
-    for k in fetch:
-        if k not in write:
-            continue
-        fb = statistics.mean(fetch[k]) * fs
-        wb = statistics.mean(write[k]) * wsc
-        tot[k] = fb + wb
-        rate = f"{(fb + wb) / (avg_us[k] * 1e3):10.1f}" if k in avg_us else f"{'':>10s}"
-        lines.append(f"{k:70s} {len(fetch[k]):4d} {fb / 1e6:10.2f} {wb / 1e6:10.2f} {rate}")
-    comb, scat, route = ("combine_kernel<false, false, 8>", "scatter_fp8_kernel<8, 2, false, false>",
-                         "route_fused_kernel<ExpertKeys>")
-    disp_b, comb_b = algorithmic_bytes(8192, 7168, 8, 256, 8192 * 8, fp8=True)
-    lines += ["", f"combine_kernel algorithmic bytes per launch: {comb_b}; counters: "
-                  f"{tot[comb]:.0f} ({tot[comb] / comb_b:.4f}x)",
-              f"dispatch (route_fused + scatter_fp8) algorithmic bytes per call: {disp_b}; "
-              f"counters: {tot[route] + tot[scat]:.0f} ({(tot[route] + tot[scat]) / disp_b:.4f}x)"]
-    with open(os.path.join(out_dir, "skewed_fp8_hbm_counters.txt"), "w") as fh:
+              "# kernel | dispatches | fetch MB | write MB (averages per dispatch, scaled)", ""]
+    headline = None
+    for wl in PROFILE_WORKLOADS:
+        fetch = per_kernel(f"{wl}_FETCH_SIZE", "bench_counter_collection.csv")
+        write = per_kernel(f"{wl}_WRITE_SIZE", "bench_counter_collection.csv")
+        lines.append(f"## {wl}: python bench.py {PROFILE_WORKLOADS[wl]}")
+        tot = {}
+        for k in fetch:
+            if k not in write or not k or k.startswith("at::") or k.startswith("__amd"):
+                continue
+            fb = statistics.mean(fetch[k]) * fs
+            wb = statistics.mean(write[k]) * wsc
+            tot[k] = fb + wb
+            lines.append(f"{k:70s} {len(fetch[k]):4d} {fb / 1e6:10.2f} {wb / 1e6:10.2f}")
+        for group, b in alg.get(wl, {}).items():
+            if all(k in tot for k in group):
+                t = sum(tot[k] for k in group)
+                lines.append(f"  {' + '.join(group)}: algorithmic {b} B, counters {t:.0f} B "
+                             f"({t / b:.4f}x)")
+                if wl == "skewed_fp8" and group == (HEADLINE_COMBINE,):
+                    headline = (fetch[HEADLINE_COMBINE], write[HEADLINE_COMBINE])
+        lines.append("")
+    with open(os.path.join(out_dir, "hbm_counters.txt"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
-    pmc_summary(os.path.join(prof_dir, "FETCH_SIZE", "bench_counter_collection.csv"),
-                os.path.join(prof_dir, "WRITE_SIZE", "bench_counter_collection.csv"),
+    pmc_summary(os.path.join(prof_dir, "skewed_fp8_FETCH_SIZE", "bench_counter_collection.csv"),
+                os.path.join(prof_dir, "skewed_fp8_WRITE_SIZE", "bench_counter_collection.csv"),
                 os.path.join(prof_dir, "cal_FETCH_SIZE", "copy_counter_collection.csv"),
                 os.path.join(prof_dir, "cal_WRITE_SIZE", "copy_counter_collection.csv"),
-                os.path.join(out_dir, "combine_skewed_fp8_pmc.json"))
+                os.path.join(out_dir, "combine_skewed_fp8_pmc.json"),
+                trace_avg_us=avg_us.get(HEADLINE_COMBINE))
 
 
 def _cpu_model():
+    """The host CPU as /proc/cpuinfo names it: model name, family / model /
+    stepping, and the clock it reports."""
+    info = {}
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            if ":" in line:
+                k, v = line.split(":", 1)
+                info.setdefault(k.strip(), v.strip())
+            if not line.strip() and info:
+                break
     except OSError:
-        pass
-    return None
+        return None
+    return (f"{info.get('model name', '?')} (family {info.get('cpu family', '?')}, model "
+            f"{info.get('model', '?')}, stepping {info.get('stepping', '?')}, "
+            f"{info.get('cpu MHz', '?')} MHz)")
 
 
-def cpu_baseline(name, T_full, sample_T, bytes_full):
-    """The oracle, as it stands, on a bounded sample of the same workload: all
-    threads OpenMP gives it on T=sample_T, and one thread on a quarter of that."""
-    import numpy as np
+def _cpu_topology():
+    """(logical CPUs in this process's affinity mask, distinct physical cores among them)."""
+    cpus = sorted(os.sched_getaffinity(0))
+    cores = set()
+    for c in cpus:
+        base = f"/sys/devices/system/cpu/cpu{c}/topology/"
+        try:
+            cores.add((open(base + "physical_package_id").read().strip(),
+                       open(base + "core_id").read().strip()))
+        except OSError:
+            cores.add(("cpu", str(c)))
+    return len(cpus), len(cores)
+
+
+def cpu_child(name, reps, threads):
+    """Runs in a child process started by cpu_baseline, with its OpenMP binding
+    environment set: the oracle as it stands on the full workload with a team
+    of `threads` (omp_set_num_threads), one warmup call then `reps` timed calls
+    of dispatch and combine (the expert step, the fp8 dequantize, is untimed).
+    Prints one JSON line, with the binding the OpenMP runtime reports."""
+    import ctypes
     import oracle
     import workloads as W
+    oracle.set_threads(threads)
+    gomp = ctypes.CDLL("libgomp.so.1")
+    bind = ["false", "true", "primary", "close", "spread"][gomp.omp_get_proc_bind()]
+    places = gomp.omp_get_num_places()
+    d = W.make_inputs(name)
+    E = d["E"]
+    fp8 = d["packed_dtype"] == "fp8"
+    disp, comb = [], []
+    for rep in range(1 + reps):
+        t0 = time.perf_counter()
+        ref = oracle.dispatch(d["x"], "bf16", d["idx"], E, packed_dt="fp8" if fp8 else None)
+        t1 = time.perf_counter()
+        y = oracle.fp8_dequant(ref["packed"], ref["scales"]) if fp8 else ref["packed"]
+        t2 = time.perf_counter()
+        oracle.combine(y, "bf16", ref["tok_map"], d["w"], "bf16")
+        t3 = time.perf_counter()
+        if rep > 0:
+            disp.append((t1 - t0) * 1e6)
+            comb.append((t3 - t2) * 1e6)
+        del ref, y
+    pair = [a + b for a, b in zip(disp, comb)]
+    print(json.dumps({"threads": oracle.get_threads(), "proc_bind": bind, "places": places,
+                      "dispatch_us": statistics.median(disp),
+                      "combine_us": statistics.median(comb), "pair_us": statistics.median(pair),
+                      "pair_us_all": pair}), flush=True)
 
-    def run(T, reps):
-        d = W.make_inputs(name, T=T)
-        E = d["E"]
-        fp8 = d["packed_dtype"] == "fp8"
-        times = []
-        for rep in range(reps):
-            t0 = time.perf_counter()
-            ref = oracle.dispatch(d["x"], "bf16", d["idx"], E, packed_dt="fp8" if fp8 else None)
-            t1 = time.perf_counter()
-            y = oracle.fp8_dequant(ref["packed"], ref["scales"]) if fp8 else ref["packed"]
-            t2 = time.perf_counter()
-            oracle.combine(y, "bf16", ref["tok_map"], d["w"], "bf16")
-            t3 = time.perf_counter()
-            if rep > 0:                  # first run warms the page cache and allocator
-                times.append((t1 - t0) + (t3 - t2))
-        return statistics.median(times) * 1e6 * (T_full / T)
 
-    threads = oracle.get_threads()
-    us_all = run(sample_T, 3)
-    t1_sample = max(sample_T // 4, 1)
-    oracle.set_threads(1)
-    try:
-        us_one = run(t1_sample, 2)
-    finally:
-        oracle.set_threads(threads)
-    return {"value": round(us_all, 1), "unit": "us/call", "cores": threads, "kind": "oracle",
-            "sample": f"{name} workload with T={sample_T} tokens, dispatch+combine timed (median "
-                      f"of 2 after 1 warmup), scaled by {T_full}/{sample_T} to one full call; "
-                      f"expert step excluded",
-            "gbps": round(bytes_full / (us_all * 1e-6) / 1e9, 2),
-            "single_thread_value": round(us_one, 1),
-            "single_thread_sample": f"T={t1_sample}, 1 warmup + 1 timed, scaled by {T_full}/{t1_sample}",
+def cpu_baseline(name, bytes_full, reps=5):
+    """The oracle, as it stands, timed on this host on the full workload: one
+    thread per physical core of the affinity mask (OMP_PLACES=cores,
+    OMP_PROC_BIND=close: never two SMT siblings), capped by the host's CPU share
+    when OMP_NUM_THREADS gives one, and again on one thread; each 1 warmup +
+    median of `reps`.  Each run is a child process, so its OpenMP runtime
+    starts with that environment."""
+    import subprocess
+    n_cpus, n_phys = _cpu_topology()
+    share = os.environ.get("OMP_NUM_THREADS", "")
+    threads = min(n_phys, int(share)) if share.isdigit() and int(share) > 0 else n_phys
+
+    def run(nthreads):
+        env = dict(os.environ, OMP_PLACES="cores", OMP_PROC_BIND="close")
+        r = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-child", name,
+                            str(reps), str(nthreads)], env=env, capture_output=True, text=True,
+                           timeout=900)
+        if r.returncode != 0:
+            raise RuntimeError(f"cpu baseline child failed:\n{r.stderr[-2000:]}")
+        return json.loads(r.stdout.strip().splitlines()[-1])
+
+    a = run(threads)
+    log(f"[bench] cpu oracle on {a['threads']} threads: {a['pair_us']:.0f} us/call")
+    one = run(1)
+    log(f"[bench] cpu oracle on {one['threads']} thread: {one['pair_us']:.0f} us/call")
+    assert one["threads"] == 1 and a["threads"] == threads, (a["threads"], one["threads"])
+    gb = lambda us: round(bytes_full / (us * 1e-6) / 1e9, 2)
+    return {"value": round(a["pair_us"], 1), "unit": "us/call", "cores": a["threads"],
+            "kind": "oracle",
+            "sample": f"the full {name} workload (every token), dispatch + combine per call; "
+                      f"1 warmup + median of {reps} calls; expert step (fp8 dequantize) untimed",
+            "dispatch_us": round(a["dispatch_us"], 1), "combine_us": round(a["combine_us"], 1),
+            "gbps": gb(a["pair_us"]),
+            "single_thread_value": round(one["pair_us"], 1),
+            "single_thread_dispatch_us": round(one["dispatch_us"], 1),
+            "single_thread_combine_us": round(one["combine_us"], 1),
+            "single_thread_gbps": gb(one["pair_us"]),
+            "omp": f"OMP_PLACES=cores OMP_PROC_BIND=close (runtime reports proc_bind "
+                   f"{a['proc_bind']}, {a['places']} places)",
+            "affinity_cpus": n_cpus, "physical_cores_in_affinity": n_phys,
+            "host_cpu_share": int(share) if share.isdigit() else None,
             "cpu_model": _cpu_model()}
 
 
@@ -622,7 +749,7 @@ def dedup_line(moe, W, args, dev, name="dedup"):
     return out
 
 
-def latency_configs(moe, W, dev, warmup=20, reps=50):
+def latency_configs(moe, W, dev, warmup=20, reps=50, names=("tiny", "decode", "prefill")):
     """Latency of the tiny, decode and prefill configurations (parity cases,
     not bench lines): HIP events around each dispatch and combine, one buffer
     set, a sleep kernel queued ahead of each pair so that host launch latency is
@@ -632,7 +759,7 @@ def latency_configs(moe, W, dev, warmup=20, reps=50):
     import torch
 
     res = {}
-    for name in ("tiny", "decode", "prefill"):
+    for name in names:
         d = W.make_inputs(name)
         T, H, E, K = d["T"], d["H"], d["E"], d["K"]
         cap = int(np.bincount(d["idx"].ravel(), minlength=E).max()) if d["layout"] == "padded" else 0
@@ -681,7 +808,17 @@ def latency_configs(moe, W, dev, warmup=20, reps=50):
                 graph.append(ev[0].elapsed_time(ev[2]) * 1e3)
         med = lambda v: round(statistics.median(v), 2)
         res[name] = {"T": T, "H": H, "E": E, "K": K, "cap": cap, "dispatch_us": med(disp),
-                     "combine_us": med(comb), "pair_us": med(both), "graph_pair_us": med(graph)}
+                     "combine_us": med(comb), "pair_us": med(both), "graph_pair_us": med(graph),
+                     "pair_us_min": round(min(both), 2), "pair_us_std": round(statistics.pstdev(both), 2)}
+        if name == "prefill":   # HBM-bound: also its bandwidth (tiny and decode are latency-bound)
+            db, cb = algorithmic_bytes(T, H, K, E, T * K, fp8=False)
+            res[name]["algorithmic_bytes"] = {"dispatch": db, "combine": cb}
+            for key, us in (("pair", med(both)), ("graph_pair", med(graph))):
+                g = (db + cb) / (us * 1e-6) / 1e9
+                res[name][f"{key}_gbps"] = round(g, 1)
+                res[name][f"{key}_pct_hbm_peak"] = round(100 * g / HBM_PEAK_GBS, 2)
+            res[name]["dispatch_gbps"] = round(db / (med(disp) * 1e-6) / 1e9, 1)
+            res[name]["combine_gbps"] = round(cb / (med(comb) * 1e-6) / 1e9, 1)
         log(f"[bench] {name}: dispatch {med(disp)} us, combine {med(comb)} us, pair {med(both)} us, "
             f"graph pair {med(graph)} us")
         del o, y, out, ow, g
@@ -725,7 +862,15 @@ def main():
     ap.add_argument("--no-fp8-combine", action="store_true",
                     help="skip the line that feeds the fp8 rows straight to moe_combine_fp8")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-sample", type=int, default=1024)
+    ap.add_argument("--cpu-reps", type=int, default=5, help="timed oracle calls per CPU run")
+    ap.add_argument("--cpu-child", nargs=3, metavar=("WORKLOAD", "REPS", "THREADS"),
+                    help=argparse.SUPPRESS)
+    ap.add_argument("--no-latency", action="store_true",
+                    help="skip the tiny / decode / prefill latency configurations")
+    ap.add_argument("--latency-reps", type=int, default=50)
+    ap.add_argument("--latency-names", default="tiny,decode,prefill",
+                    help="configurations timed by the latency leg (comma separated)")
+    ap.add_argument("--only-dedup", action="store_true", help="only the dedup line (one JSON line)")
     ap.add_argument("--latency-profile-text", nargs=2, metavar=("PROF_DIR", "OUT_DIR"),
                     help="write the text summary of the rocprofv3 run of --latency-configs")
     ap.add_argument("--latency-configs", action="store_true",
@@ -738,6 +883,9 @@ def main():
                     help="summarize rocprofv3 FETCH_SIZE / WRITE_SIZE csvs into OUT (json)")
     args = ap.parse_args()
 
+    if args.cpu_child:
+        cpu_child(args.cpu_child[0], int(args.cpu_child[1]), int(args.cpu_child[2]))
+        return
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary)
         return
@@ -764,8 +912,13 @@ def main():
     if args.calibrate_copy:
         calibrate_copy(args.steps)
         return
+    names = tuple(n for n in args.latency_names.split(",") if n)
     if args.latency_configs:
-        print(json.dumps({"latency_configs": latency_configs(moe, W, dev)}), flush=True)
+        print(json.dumps({"latency_configs": latency_configs(moe, W, dev, reps=args.latency_reps,
+                                                             names=names)}), flush=True)
+        return
+    if args.only_dedup:
+        print(json.dumps({"dedup": dedup_line(moe, W, args, dev)}), flush=True)
         return
     name = args.workload
     r = measure(moe, W, name, args, dev, graphs=not args.no_graph)
@@ -778,7 +931,8 @@ def main():
     c_avg = r["combine_us_mean"]
     roof_gbs = comb_b / (c_avg * 1e-6) / 1e9
     khash = source_hash(COMBINE_SOURCES)
-    traffic = stored_traffic(khash)
+    prof = stored_profile(khash)
+    traffic = prof.get("traffic_bytes_per_launch")
     log(f"[bench] dispatch {d_us:.1f} us ({disp_gbs:.0f} GB/s)  combine {c_us:.1f} us "
         f"({comb_gbs:.0f} GB/s)  total {t_us:.1f} us ({gbs:.0f} GB/s, {100 * gbs / HBM_PEAK_GBS:.1f}% "
         f"of peak)  wall {r['wall_ms'] * 1e3:.1f} us/step")
@@ -839,11 +993,14 @@ def main():
     copy_gbs = copy_ceiling(moe, dev)
     log(f"[bench] 16-byte streaming copy of 1 GiB: {copy_gbs:.0f} GB/s (read + write)")
 
+    lat = None
+    if not args.no_latency:
+        lat = latency_configs(moe, W, dev, reps=args.latency_reps, names=names)
+
     cpu = None
     if not args.no_cpu:
-        log(f"[bench] cpu oracle baseline on T={args.cpu_sample} sample ...")
-        cpu = cpu_baseline(name, r["T"], args.cpu_sample, r["disp_b"] + r["comb_b"])
-        log(f"[bench] cpu oracle: {cpu['value']} us/call on {cpu['cores']} threads")
+        log(f"[bench] cpu oracle baseline on the full {name} workload ...")
+        cpu = cpu_baseline(name, r["disp_b"] + r["comb_b"], reps=args.cpu_reps)
 
     line = {
         "metric": METRIC,
@@ -862,7 +1019,10 @@ def main():
                    "routing": "zipf1.2" if r["routing"] == "zipf" else "uniform",
                    "payload": "fp8_e4m3+f32_scale_per_128" if r["fp8"] else "bf16",
                    "combine": "bf16_in_f32_acc_bf16_out", "layout": "compact",
-                   "buffer_sets": args.sets},
+                   "buffer_sets": args.sets,
+                   "dtypes": {"x": "bf16", "payload": "fp8_e4m3" if r["fp8"] else "bf16",
+                              "scales": "f32" if r["fp8"] else None, "y": "bf16",
+                              "arithmetic": "f32", "accumulate": "f32", "out": "bf16"}},
         "achieved_gbps": round(gbs, 1),
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "pct_copy_ceiling": round(100 * gbs / copy_gbs, 2),
@@ -870,6 +1030,9 @@ def main():
         "pair_us_min": round(r["pair_us_min"], 2),
         "pair_us_std": round(r["pair_us_std"], 2),
         "graph_pair_us": round(r["graph_pair_us"], 2) if "graph_pair_us" in r else None,
+        "pct_hbm_peak_graph": (round(100 * total_b / (r["graph_pair_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 2)
+                               if "graph_pair_us" in r else None),
+        "pct_hbm_peak_wall": round(100 * total_b / (r["wall_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
         "graph_pair_us_min": round(r["graph_pair_us_min"], 2) if "graph_pair_us" in r else None,
         "dispatch_us": round(d_us, 2),
         "combine_us": round(c_us, 2),
@@ -879,12 +1042,21 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "combine_kernel", "achieved": round(roof_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(roof_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "bytes_per_launch": comb_b,
-                     "avg_launch_us": round(c_avg, 2)},
+                     "avg_launch_us": round(c_avg, 2),
+                     "avg_launch_us_source": "HIP events around each combine launch of the timed "
+                                             "region, on its stream (includes event overhead)",
+                     "kernel_trace": ({"avg_launch_us": round(prof["trace_avg_us"], 2),
+                                       "frac": round(comb_b / (prof["trace_avg_us"] * 1e-6) / 1e9
+                                                     / HBM_PEAK_GBS, 4),
+                                       "source": "profiles/skewed_fp8_kernel_trace.txt "
+                                                 "(rocprofv3 kernel trace, same kernel source)"}
+                                      if prof.get("trace_avg_us") else None)},
         "secondary": sec,
         "fp8_combine": f8,
         "fp4_payload": f4,
         "dispatch_variants": dv,
         "dedup": dd,
+        "latency_configs": lat,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
