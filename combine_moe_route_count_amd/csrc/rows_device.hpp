@@ -39,15 +39,20 @@ __device__ __forceinline__ void settle(u32x4 (&v)[N]) {
     for (int i = 0; i < N; ++i) asm volatile("" : "+v"(v[i]));
 }
 
-// Copy one row of nvec 16-byte vectors (already holding pass 0 in val) to up
-// to D destination rows with store policy POL; passes after the first reload
-// from src.
+// The 16-byte vectors [v0, v1) of a row: the part of it one workgroup moves.
+struct VecRange {
+    int v0, v1;
+};
+
+// Copy the vectors r of one row (already holding pass 0 in val) to up to D
+// destination rows with store policy POL; passes after the first reload from
+// src.
 template <int DMAX, int VPT, int POL>
-__device__ __forceinline__ void store_row_copies(const char* src, int nvec, char* dst,
+__device__ __forceinline__ void store_row_copies(const char* src, VecRange r, char* dst,
                                                  int64_t row_bytes, const int (&rows)[DMAX], int D,
                                                  u32x4 (&val)[VPT], int tid, int nthreads) {
     const int step = VPT * nthreads;
-    for (int base = 0;;) {
+    for (int base = r.v0;;) {
         // Every store below is conditional and reads loaded registers; without
         // this one explicit use the compiler loses count of the loads at each
         // join and waits for vmcnt(0) before every store, i.e. for the previous
@@ -61,26 +66,26 @@ __device__ __forceinline__ void store_row_copies(const char* src, int nvec, char
 #pragma unroll
             for (int i = 0; i < VPT; ++i) {
                 const int v = base + tid + i * nthreads;
-                if (v < nvec) out.st16(v * 16, val[i]);
+                if (v < r.v1) out.st16(v * 16, val[i]);
             }
         }
         base += step;
-        if (base >= nvec) break;
+        if (base >= r.v1) break;
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
             const int v = base + tid + i * nthreads;
-            if (v < nvec) val[i] = ld16_stream(src + (int64_t)v * 16);
+            if (v < r.v1) val[i] = ld16_stream(src + (int64_t)v * 16);
         }
     }
 }
 
 template <int VPT>
-__device__ __forceinline__ void load_first_pass(const char* src, int nvec, u32x4 (&val)[VPT],
+__device__ __forceinline__ void load_first_pass(const char* src, VecRange r, u32x4 (&val)[VPT],
                                                 int tid, int nthreads) {
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-        const int v = tid + i * nthreads;
-        if (v < nvec) val[i] = ld16_stream(src + (int64_t)v * 16);
+        const int v = r.v0 + tid + i * nthreads;
+        if (v < r.v1) val[i] = ld16_stream(src + (int64_t)v * 16);
     }
 }
 

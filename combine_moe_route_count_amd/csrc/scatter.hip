@@ -84,33 +84,33 @@ struct LookupRows {
     }
 };
 
-// get_rows(t, rows) runs after the first loads of the row are issued, so
-// their latency overlaps it.
+// The vectors of chunk c of a row of nvec vectors cut into chunks of C.
+__device__ __forceinline__ VecRange chunk_range(int c, int C, int nvec) {
+    return VecRange{c * C, min(nvec, c * C + C)};
+}
+
+// Moves the vectors r of token t's row; get_rows(t, rows) runs after the
+// first loads of the row are issued, so their latency overlaps it.  first:
+// this workgroup holds the row's first chunk and forwards the scale row.
 template <int DMAX, int VPT, bool SC, class RowsFn>
 __device__ __forceinline__ void scatter_copy_item(const ScatterArgs& a, int64_t t, int nth,
-                                                  const RowsFn& get_rows) {
+                                                  VecRange r, bool first, const RowsFn& get_rows) {
     const int tid = threadIdx.x;
     const int64_t row_bytes = a.H * a.x_bytes;
-    const int nvec = (int)(row_bytes / 16);
     const char* src = (const char*)a.x + t * row_bytes;
 
     u32x4 val[VPT];
-    load_first_pass<VPT>(src, nvec, val, tid, nth);
+    load_first_pass<VPT>(src, r, val, tid, nth);
 
     int rows[DMAX];
     get_rows(t, rows);
     // scales first: loading them after the row stores would reuse registers the
     // stores still read, and the compiler would wait for every store first
-    if (SC) forward_scales<DMAX>(a, t, rows, nth);
+    if (SC && first) forward_scales<DMAX>(a, t, rows, nth);
     // SC: pre-quantized fp8 rows; otherwise bf16 / f32 row copies
-    store_row_copies<DMAX, VPT, SC ? kStoreThrough : kStorePlain>(src, nvec, (char*)a.packed,
+    store_row_copies<DMAX, VPT, SC ? kStoreThrough : kStorePlain>(src, r, (char*)a.packed,
                                                                    row_bytes, rows, a.slot.K, val,
                                                                    tid, nth);
-}
-
-template <int DMAX, int VPT, bool REPLAY, bool SC>
-__device__ __forceinline__ void scatter_copy_kernel_item(const ScatterArgs& a, int64_t t, int nth) {
-    scatter_copy_item<DMAX, VPT, SC>(a, t, nth, LookupRows<DMAX, REPLAY>{a});
 }
 
 // ---------------------------------------------------------------------------
@@ -191,16 +191,16 @@ __device__ __forceinline__ void scatter_fp8_item(const ScatterArgs& a, int64_t t
 // dedup stage 1: one copy of x[t] per (t, r) in the token's rank mask
 // ---------------------------------------------------------------------------
 template <int DMAX, int VPT>
-__device__ __forceinline__ void recv_copy_kernel_item(const RecvArgs& a, int64_t t, int nth) {
+__device__ __forceinline__ void recv_copy_kernel_item(const RecvArgs& a, int64_t t, int nth,
+                                                      VecRange vr, bool meta) {
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
     const int R = a.R;
     const int64_t row_bytes = a.H * a.x_bytes;
-    const int nvec = (int)(row_bytes / 16);
     const char* src = (const char*)a.x + t * row_bytes;
 
     u32x4 val[VPT];
-    load_first_pass<VPT>(src, nvec, val, tid, nth);
+    load_first_pass<VPT>(src, vr, val, tid, nth);
 
     int my_row = -1;
     if (lane < R) {
@@ -211,14 +211,14 @@ __device__ __forceinline__ void recv_copy_kernel_item(const RecvArgs& a, int64_t
             my_row = row < a.recv_rows ? (int)row : -1;
         }
     }
-    if (tid < R) {
+    if (tid < R && meta) {
         a.rank_slot[t * R + tid] = my_row;
         if (my_row >= 0) a.recv_src[my_row] = (int32_t)t;
     }
     // Entries that no recv row carries (no expert, an invalid id, or a recv row
     // past recv_rows) get their -1 here; the expansion, which walks the recv
     // rows, writes every other entry.  Rank of a valid e: e / (E/R).
-    {
+    if (meta) {
         int e = -1;
         if (tid < a.K) e = a.idx[t * a.K + tid];
         const bool valid = tid < a.K && e >= 0 && e < a.E;
@@ -228,7 +228,7 @@ __device__ __forceinline__ void recv_copy_kernel_item(const RecvArgs& a, int64_t
     }
     int rows[DMAX];
     broadcast_rows<DMAX>(my_row, rows);
-    store_row_copies<DMAX, VPT, kStorePlain>(src, nvec, (char*)a.recv_x, row_bytes, rows, R, val,
+    store_row_copies<DMAX, VPT, kStorePlain>(src, vr, (char*)a.recv_x, row_bytes, rows, R, val,
                                              tid, nth);
 }
 
@@ -244,18 +244,18 @@ __device__ __forceinline__ void recv_copy_kernel_item(const RecvArgs& a, int64_t
 // entries) took 552 us against about 525 for this order at T=16384 H=4096 E=64
 // K=6 R=8 f32.
 template <int KMAX, int VPT>
-__device__ __forceinline__ void expand_kernel_item(const ExpandArgs& a, int64_t j, int nth) {
+__device__ __forceinline__ void expand_kernel_item(const ExpandArgs& a, int64_t j, int nth,
+                                                   VecRange vr, bool meta) {
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
     const int K = a.slot.K;
     const int R = a.R;
     const int er = a.slot.E / R;
     const int64_t row_bytes = a.H * a.x_bytes;
-    const int nvec = (int)(row_bytes / 16);
     const char* src = (const char*)a.recv_x + j * row_bytes;
 
     u32x4 val[VPT];
-    load_first_pass<VPT>(src, nvec, val, tid, nth);
+    load_first_pass<VPT>(src, vr, val, tid, nth);
 
     // rank of row j: the last segment starting at or before j (empty segments
     // start where the next one does, so they are never the last)
@@ -273,15 +273,16 @@ __device__ __forceinline__ void expand_kernel_item(const ExpandArgs& a, int64_t 
             my_row = entry_row(a.slot, f);
         }
     }
-    // every wave needs the rows for its broadcast; the first wave writes them
-    if (tid < K && on_rank) {
+    // every wave needs the rows for its broadcast; the first wave of the row's
+    // first chunk writes them
+    if (tid < K && on_rank && meta) {
         const int64_t f = (int64_t)t * K + tid;
         a.tok_map[f] = my_row;
         if (my_row >= 0) a.packed_src[my_row] = t;
     }
     int rows[KMAX];
     broadcast_rows<KMAX>(my_row, rows);
-    store_row_copies<KMAX, VPT, kStoreThrough>(src, nvec, (char*)a.packed, row_bytes, rows, K, val,
+    store_row_copies<KMAX, VPT, kStoreThrough>(src, vr, (char*)a.packed, row_bytes, rows, K, val,
                                                tid, nth);
 }
 
@@ -292,10 +293,19 @@ __device__ __forceinline__ void expand_kernel_item(const ExpandArgs& a, int64_t 
 // 16-bit field that gfx9 can only read with a vector load, which the compiler
 // repeats after every store it cannot prove disjoint and then waits for with
 // vmcnt(0), i.e. for every store in flight.
+// nch workgroups per row (chunks of C vectors); chunk 0 writes the row's
+// routing outputs.
 template <int DMAX, int VPT, bool REPLAY, bool SC>
-__global__ __launch_bounds__(kCopyThreads) void scatter_copy_kernel(ScatterArgs a, int nth) {
-    for (int64_t t = blockIdx.x; t < a.T; t += gridDim.x)
-        scatter_copy_kernel_item<DMAX, VPT, REPLAY, SC>(a, t, nth);
+__global__ __launch_bounds__(kCopyThreads) void scatter_copy_kernel(ScatterArgs a, int nth, int nch,
+                                                                    int C) {
+    const int nvec = (int)(a.H * a.x_bytes / 16);
+    const int64_t items = a.T * nch;
+    for (int64_t wi = blockIdx.x; wi < items; wi += gridDim.x) {
+        const int64_t t = wi / nch;
+        const int c = (int)(wi - t * nch);
+        scatter_copy_item<DMAX, VPT, SC>(a, t, nth, chunk_range(c, C, nvec), c == 0,
+                                         LookupRows<DMAX, REPLAY>{a, c == 0});
+    }
 }
 template <int DMAX, int UPT, bool REPLAY, bool FP4>
 __global__ __launch_bounds__(kCopyThreads) void scatter_fp8_kernel(ScatterArgs a, int nth, int nch,
@@ -309,15 +319,27 @@ __global__ __launch_bounds__(kCopyThreads) void scatter_fp8_kernel(ScatterArgs a
     }
 }
 template <int DMAX, int VPT>
-__global__ __launch_bounds__(kCopyThreads) void recv_copy_kernel(RecvArgs a, int nth) {
-    for (int64_t t = blockIdx.x; t < a.T; t += gridDim.x) recv_copy_kernel_item<DMAX, VPT>(a, t, nth);
+__global__ __launch_bounds__(kCopyThreads) void recv_copy_kernel(RecvArgs a, int nth, int nch, int C) {
+    const int nvec = (int)(a.H * a.x_bytes / 16);
+    const int64_t items = a.T * nch;
+    for (int64_t wi = blockIdx.x; wi < items; wi += gridDim.x) {
+        const int64_t t = wi / nch;
+        const int c = (int)(wi - t * nch);
+        recv_copy_kernel_item<DMAX, VPT>(a, t, nth, chunk_range(c, C, nvec), c == 0);
+    }
 }
 template <int KMAX, int VPT>
-__global__ __launch_bounds__(kCopyThreads) void expand_kernel(ExpandArgs a, int nth) {
+__global__ __launch_bounds__(kCopyThreads) void expand_kernel(ExpandArgs a, int nth, int nch, int C) {
     // rows written by the recv copy: the uncapped total, clipped to recv_rows
     const int64_t total = a.recv_off[a.R];
     const int64_t n = total < a.recv_rows ? total : a.recv_rows;
-    for (int64_t j = blockIdx.x; j < n; j += gridDim.x) expand_kernel_item<KMAX, VPT>(a, j, nth);
+    const int nvec = (int)(a.H * a.x_bytes / 16);
+    const int64_t items = n * nch;
+    for (int64_t wi = blockIdx.x; wi < items; wi += gridDim.x) {
+        const int64_t j = wi / nch;
+        const int c = (int)(wi - j * nch);
+        expand_kernel_item<KMAX, VPT>(a, j, nth, chunk_range(c, C, nvec), c == 0);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -406,10 +428,11 @@ __global__ __launch_bounds__(kSmallThreads) void dispatch_small_kernel(ScatterAr
         return;
     }
     const SmallRows<DMAX> rows{a, nbits, run_all, rank_lds, key_lds, off_lds, flags_lds, wave_sums};
+    const VecRange whole{0, (int)(a.H * a.x_bytes / 16)};
     if constexpr (MODE == SmallMode::Copy)
-        scatter_copy_item<DMAX, 4, false>(a, t, kSmallThreads, rows);
+        scatter_copy_item<DMAX, 4, false>(a, t, kSmallThreads, whole, true, rows);
     else if constexpr (MODE == SmallMode::CopyScales)
-        scatter_copy_item<DMAX, 4, true>(a, t, kSmallThreads, rows);
+        scatter_copy_item<DMAX, 4, true>(a, t, kSmallThreads, whole, true, rows);
     else
         scatter_fp8_item<DMAX, 2, MODE == SmallMode::Fp4>(a, t, kSmallThreads, 0, (int)(a.H / 16),
                                                           rows);
@@ -548,12 +571,48 @@ inline Fp8Split fp8_split(int64_t H, bool fp4) {
     return sp;
 }
 
+// Split of a row over the workgroups of a bit-copy kernel: nch workgroups per
+// row of nvec 16-byte vectors, C vectors each, and at most wgs_per_cu of them
+// resident on a CU (an LDS reservation; 0: no cap).
+struct CopySplit {
+    int nch;
+    int C;
+    int threads;
+    size_t lds;
+};
+inline CopySplit copy_split(int nvec, int chunks, int wgs_per_cu) {
+    CopySplit sp;
+    sp.nch = chunks < 1 ? 1 : (chunks > nvec ? nvec : chunks);
+    sp.C = (nvec + sp.nch - 1) / sp.nch;
+    sp.nch = (nvec + sp.C - 1) / sp.C;   // no empty chunk
+    sp.threads = copy_threads<4>(sp.C);
+    sp.lds = wgs_per_cu > 0 ? kLdsPerCu / wgs_per_cu : 0;
+    return sp;
+}
+// Token-row copies (bf16, f32, pre-quantized fp8): one uncapped workgroup per
+// row (two or four chunks, or caps of 4-7 per CU, measured 0-8 us slower on the
+// T=8192 H=7168 K=8 bf16 dispatch and the prefill one).  The dedup recv copy:
+// two workgroups per 16 KB f32 row.  The dedup expansion: whole recv rows, at
+// most 4 workgroups per CU; in recv-row order the resident workgroups then
+// write a narrower band of the rank's expert segments (T=16384 H=4096 E=64 K=6
+// R=8: dedup dispatch 788 -> 766 us with the cap, 760 us with the split recv
+// copy; caps of 3 or 6 per CU, or chunked expansion rows, were slower).
+constexpr int kCopyChunks = 1, kCopyWgsPerCu = 0;
+constexpr int kRecvChunks = 2, kRecvWgsPerCu = 0;
+constexpr int kExpandChunks = 1, kExpandWgsPerCu = 4;
+
+inline dim3 copy_grid(int64_t items) {
+    return dim3((unsigned)(items < kMaxGrid ? items : kMaxGrid));
+}
+
 template <bool REPLAY, bool SC>
 struct CopyMode {
     template <int D, int V>
     struct Launch {
-        static void go(dim3 g, int th, const ScatterArgs& a, hipStream_t s) {
-            scatter_copy_kernel<D, V, REPLAY, SC><<<g, dim3(th), 0, s>>>(a, th);
+        static void go(dim3, int, const ScatterArgs& a, hipStream_t s) {
+            const CopySplit sp = copy_split((int)(a.H * a.x_bytes / 16), kCopyChunks, kCopyWgsPerCu);
+            scatter_copy_kernel<D, V, REPLAY, SC>
+                <<<copy_grid(a.T * sp.nch), dim3(sp.threads), sp.lds, s>>>(a, sp.threads, sp.nch, sp.C);
         }
     };
 };
@@ -572,14 +631,18 @@ struct Fp8Mode {
 };
 template <int D, int V>
 struct LaunchRecv {
-    static void go(dim3 g, int th, const RecvArgs& a, hipStream_t s) {
-        recv_copy_kernel<D, V><<<g, dim3(th), 0, s>>>(a, th);
+    static void go(dim3, int, const RecvArgs& a, hipStream_t s) {
+        const CopySplit sp = copy_split((int)(a.H * a.x_bytes / 16), kRecvChunks, kRecvWgsPerCu);
+        recv_copy_kernel<D, V>
+            <<<copy_grid(a.T * sp.nch), dim3(sp.threads), sp.lds, s>>>(a, sp.threads, sp.nch, sp.C);
     }
 };
 template <int D, int V>
 struct LaunchExpand {
-    static void go(dim3 g, int th, const ExpandArgs& a, hipStream_t s) {
-        expand_kernel<D, V><<<g, dim3(th), 0, s>>>(a, th);
+    static void go(dim3, int, const ExpandArgs& a, hipStream_t s) {
+        const CopySplit sp = copy_split((int)(a.H * a.x_bytes / 16), kExpandChunks, kExpandWgsPerCu);
+        expand_kernel<D, V><<<copy_grid(a.recv_rows * sp.nch), dim3(sp.threads), sp.lds, s>>>(
+            a, sp.threads, sp.nch, sp.C);
     }
 };
 
