@@ -496,17 +496,24 @@ def measure(moe, W, name, args, dev, graphs=True, y_fp8=False, fp4=False):
     torch.cuda.synchronize()
     log(f"[bench] {name}: warmup {args.warmup} done")
 
-    n_ev = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_ev)]
+    # wall clock over exactly `steps` back-to-back steps, no event markers
+    # between them (each marker leaves the GPU idle for several microseconds)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, ev[i])
+        step(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    wall_ms = (t1 - t0) * 1e3 / args.steps
+
+    n_ev = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_ev)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i, ev[i])
+    torch.cuda.synchronize()
     log(f"[bench] {name}: timed {args.steps} steps done")
     pair_us = [ev[i][0].elapsed_time(ev[i][1]) * 1e3 for i in range(n_ev)]
-    wall_ms = (t1 - t0) * 1e3 / args.steps
 
     evb = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_ev)]
     for i in range(args.steps):
@@ -572,8 +579,34 @@ def measure(moe, W, name, args, dev, graphs=True, y_fp8=False, fp4=False):
         for st_, ref in zip(sets, eager_out):
             assert torch.equal(st_["out"].view(torch.int16), ref.view(torch.int16)), \
                 "split graph replay output differs from the eager output"
-        del gs, gd, gc
-        log(f"[bench] {name}: graph replays done, outputs equal to eager")
+        # one graph holding a step on every buffer set: each launch of a graph
+        # leaves the GPU idle for several microseconds before its first kernel
+        # (none between its nodes), which a graph of several steps shares out
+        for st_ in sets:
+            st_["out"].zero_()
+        with torch.cuda.stream(cs):
+            gm = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gm, stream=cs):
+                for i in range(len(sets)):
+                    step(i)
+        torch.cuda.synchronize()
+        for _ in range(max(1, args.warmup // len(sets))):
+            gm.replay()
+        n_m = max(2, args.steps // len(sets))
+        evm = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_m)]
+        for i in range(n_m):
+            evm[i][0].record(stream)
+            gm.replay()
+            evm[i][1].record(stream)
+        torch.cuda.synchronize()
+        graph_multi_us = [e[0].elapsed_time(e[1]) * 1e3 / len(sets) for e in evm]
+        for st_, ref in zip(sets, eager_out):
+            assert torch.equal(st_["out"].view(torch.int16), ref.view(torch.int16)), \
+                "multi-step graph replay output differs from the eager output"
+        del gs, gd, gc, gm
+        log(f"[bench] {name}: graph replays done, outputs equal to eager; pair per graph "
+            f"{statistics.median(graph_us[1:]):.1f} us, {len(sets)} pairs per graph "
+            f"{statistics.median(graph_multi_us[1:]):.1f} us per pair")
 
     # drop the first timed round (start transient)
     tail = lambda v: v[1:] if len(v) > 2 else v
@@ -596,6 +629,9 @@ def measure(moe, W, name, args, dev, graphs=True, y_fp8=False, fp4=False):
                  graph_pair_us_std=statistics.pstdev(tail(graph_us)))
         r["timing"]["graph"] = {"pair": spread(graph_us), "dispatch": spread(graph_disp_us),
                                 "combine": spread(graph_comb_us)}
+        r["timing"]["graph_multi_step"] = {"steps_per_graph": len(sets),
+                                           "pair": spread(graph_multi_us)}
+        r["graph_multi_pair_us"] = statistics.median(tail(graph_multi_us))
     del sets
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
@@ -1032,6 +1068,11 @@ def main():
         "graph_pair_us": round(r["graph_pair_us"], 2) if "graph_pair_us" in r else None,
         "pct_hbm_peak_graph": (round(100 * total_b / (r["graph_pair_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 2)
                                if "graph_pair_us" in r else None),
+        "graph_multi_step_pair_us": (round(r["graph_multi_pair_us"], 2)
+                                     if "graph_multi_pair_us" in r else None),
+        "pct_hbm_peak_graph_multi_step": (round(100 * total_b / (r["graph_multi_pair_us"] * 1e-6) / 1e9
+                                                / HBM_PEAK_GBS, 2)
+                                          if "graph_multi_pair_us" in r else None),
         "pct_hbm_peak_wall": round(100 * total_b / (r["wall_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
         "graph_pair_us_min": round(r["graph_pair_us_min"], 2) if "graph_pair_us" in r else None,
         "dispatch_us": round(d_us, 2),
