@@ -789,8 +789,10 @@ def latency_configs(moe, W, dev, warmup=20, reps=50, names=("tiny", "decode", "p
     """Latency of the tiny, decode and prefill configurations (parity cases,
     not bench lines): HIP events around each dispatch and combine, one buffer
     set, a sleep kernel queued ahead of each pair so that host launch latency is
-    not timed; then the pair captured as one graph and replayed the same way.
-    Expert stand-in: identity (the packed rows are the combine's input)."""
+    not timed; then the pair captured as one graph and replayed the same way;
+    then the host side: time inside each call and the wall clock of a round
+    with its synchronisation.  Expert stand-in: identity (the packed rows are
+    the combine's input)."""
     import numpy as np
     import torch
 
@@ -842,10 +844,48 @@ def latency_configs(moe, W, dev, warmup=20, reps=50, names=("tiny", "decode", "p
             torch.cuda.synchronize()
             if i >= warmup:
                 graph.append(ev[0].elapsed_time(ev[2]) * 1e3)
+        # host time inside each call (the pages' hdis / hcom) and the host wall
+        # clock of a round with its synchronisation (hwal): through the Python
+        # binding, and through bare ctypes calls of the C ABI with prepared
+        # arguments (what a C caller pays: argument checks and the launches)
+        L = moe.load()
+        P = moe._lib.ptr
+        st_ = moe._lib._stream(dev)
+        pk = moe._lib.dtype_code(x.dtype)
+        d_args = (P(x), pk, T, H, P(idx), K, E, cap, o.packed.shape[0], P(o.packed), pk, None,
+                  P(o.packed_cnt), P(o.packed_off), P(o.packed_src), P(o.tok_map), P(o.stats),
+                  P(ws), ws.numel(), st_)
+        c_args = (P(y), pk, y.shape[0], H, P(o.tok_map), P(w), T, K, 0, None, P(out), pk, P(ow), st_)
+        hd, hc, hw, rd, rc = [], [], [], [], []
+        for i in range(warmup + reps):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            moe.dispatch(x, idx, E, cap=cap, out=o, ws=ws)
+            t1 = time.perf_counter()
+            moe.combine(y, o.tok_map, w, out=out, out_weights=ow)
+            t2 = time.perf_counter()
+            torch.cuda.synchronize()
+            t3 = time.perf_counter()
+            u0 = time.perf_counter()
+            sd = L.moe_dispatch(*d_args)
+            u1 = time.perf_counter()
+            sc = L.moe_combine(*c_args)
+            u2 = time.perf_counter()
+            assert sd == 0 and sc == 0
+            if i >= warmup:
+                hd.append((t1 - t0) * 1e6)
+                hc.append((t2 - t1) * 1e6)
+                hw.append((t3 - t0) * 1e6)
+                rd.append((u1 - u0) * 1e6)
+                rc.append((u2 - u1) * 1e6)
+        torch.cuda.synchronize()
         med = lambda v: round(statistics.median(v), 2)
+        host = {"dispatch_us": med(hd), "combine_us": med(hc), "round_wall_us": med(hw),
+                "dispatch_abi_us": med(rd), "combine_abi_us": med(rc)}
         res[name] = {"T": T, "H": H, "E": E, "K": K, "cap": cap, "dispatch_us": med(disp),
                      "combine_us": med(comb), "pair_us": med(both), "graph_pair_us": med(graph),
-                     "pair_us_min": round(min(both), 2), "pair_us_std": round(statistics.pstdev(both), 2)}
+                     "pair_us_min": round(min(both), 2), "pair_us_std": round(statistics.pstdev(both), 2),
+                     "host_us": host}
         if name == "prefill":   # HBM-bound: also its bandwidth (tiny and decode are latency-bound)
             db, cb = algorithmic_bytes(T, H, K, E, T * K, fp8=False)
             res[name]["algorithmic_bytes"] = {"dispatch": db, "combine": cb}
@@ -856,7 +896,9 @@ def latency_configs(moe, W, dev, warmup=20, reps=50, names=("tiny", "decode", "p
             res[name]["dispatch_gbps"] = round(db / (med(disp) * 1e-6) / 1e9, 1)
             res[name]["combine_gbps"] = round(cb / (med(comb) * 1e-6) / 1e9, 1)
         log(f"[bench] {name}: dispatch {med(disp)} us, combine {med(comb)} us, pair {med(both)} us, "
-            f"graph pair {med(graph)} us")
+            f"graph pair {med(graph)} us; host in dispatch {host['dispatch_us']} us "
+            f"(bare ABI {host['dispatch_abi_us']}), in combine {host['combine_us']} us "
+            f"(bare ABI {host['combine_abi_us']}), round wall {host['round_wall_us']} us")
         del o, y, out, ow, g
         torch.cuda.empty_cache()
     return res
