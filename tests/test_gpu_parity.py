@@ -448,6 +448,128 @@ def test_grid_stride_wrap_past_max_grid():
     np.testing.assert_array_equal(host(ow), ew)
 
 
+@pytest.mark.parametrize("payload,H", [("bf16", 7168), ("fp8", 16384)])
+def test_byte_offsets_past_4gib(payload, H):
+    """Packed buffers larger than 4 GiB (320000 rows of 14 KB bf16 or 16 KB e4m3):
+    the rows at the end lie past 2^32 bytes, so any 32-bit row offset would land
+    elsewhere.  Routing outputs in full (numpy's stable sort states the slot
+    rule independently); rows, scales and the combine on sampled rows and
+    tokens, the last ones included, against the oracle."""
+    T, K, E = 40000, 8, 256
+    rng = np.random.default_rng(44)
+    idx = np.argsort(rng.random((T, E)), axis=1)[:, :K].astype(np.int32)
+    x = rng.integers(0, 1 << 16, size=(T, H), dtype=np.uint16)
+    x[(x & 0x7F80) == 0x7F80] = 0x3F80            # finite values only
+    fp8 = payload == "fp8"
+    note(f"byte offsets past 4 GiB: {payload} T={T} K={K} E={E} H={H}")
+    o = gpu_dispatch(dev_bf16(x), idx, E, fp8=fp8)
+    row_bytes = H if fp8 else 2 * H
+    assert T * K * row_bytes > (1 << 32)
+    flat = idx.ravel()
+    order = np.argsort(flat, kind="stable")
+    tm = np.empty(T * K, np.int64)
+    tm[order] = np.arange(T * K)
+    np.testing.assert_array_equal(host(o.tok_map).ravel(), tm)
+    np.testing.assert_array_equal(host(o.packed_src), (order // K).astype(np.int32))
+    rc, ro, _ = oracle.route_count(idx, E)
+    np.testing.assert_array_equal(host(o.packed_cnt), rc)
+    np.testing.assert_array_equal(host(o.packed_off), ro)
+    # sampled rows: the last 2000 (all past 2^32 bytes) and 2000 spread out
+    rows = np.unique(np.concatenate([np.arange(T * K - 2000, T * K),
+                                     rng.integers(0, T * K, 2000)]))
+    assert rows[-1] * row_bytes > (1 << 32)
+    src = order[rows] // K
+    got = host(o.packed[torch.from_numpy(rows).to(DEV)])
+    if fp8:
+        q, sc = oracle.fp8_pack_rows(x[src])
+        np.testing.assert_array_equal(got, q)
+        np.testing.assert_array_equal(host(o.scales[torch.from_numpy(rows).to(DEV)]).view(np.uint32),
+                                      sc.view(np.uint32))
+    else:
+        np.testing.assert_array_equal(got.view(np.uint16), x[src])
+    # combine of sampled tokens (the last ones read the rows past 2^32 bytes):
+    # the oracle combines the same tokens over the rows they name
+    w = rng.random((T, K)).astype(np.float32)
+    if fp8:
+        out, ow = moe.combine_fp8(o.packed, o.scales, o.tok_map, dev(w))
+    else:
+        out, ow = moe.combine(o.packed, o.tok_map, dev(w))
+    torch.cuda.synchronize()
+    toks = np.unique(np.concatenate([order[-2000:] // K, rng.integers(0, T, 1000)]))
+    sub_rows = np.unique(tm.reshape(T, K)[toks].ravel())
+    remap = {int(r): i for i, r in enumerate(sub_rows)}
+    sub_tm = np.vectorize(lambda r: remap[int(r)])(tm.reshape(T, K)[toks]).astype(np.int64)
+    y_sub = host(o.packed[torch.from_numpy(sub_rows).to(DEV)])
+    if fp8:
+        s_sub = host(o.scales[torch.from_numpy(sub_rows).to(DEV)])
+        eo, ew = oracle.combine_fp8(y_sub, s_sub, sub_tm, w[toks], "bf16")
+    else:
+        eo, ew = oracle.combine(y_sub.view(np.uint16), "bf16", sub_tm, w[toks], "bf16")
+    assert _check_combine(host(out[torch.from_numpy(toks).to(DEV)]), eo, "bf16")
+    np.testing.assert_array_equal(host(ow)[toks], ew)
+
+
+def test_dedup_byte_offsets_past_4gib():
+    """Dedup dispatch and combine with recv and packed buffers larger than 4 GiB
+    (about 272000 recv rows and 360000 packed rows of 16 KB f32): recv and
+    packed rows at the end lie past 2^32 bytes.  Routing outputs in full
+    against numpy statements of the rank-mask and slot rules, rows and the
+    fused and two-stage combines on samples against the oracle."""
+    T, K, E, R, H = 60000, 6, 64, 8, 4096
+    er = E // R
+    rng = np.random.default_rng(45)
+    idx = np.argsort(rng.random((T, E)), axis=1)[:, :K].astype(np.int32)
+    x = rng.standard_normal((T, H), dtype=np.float32)
+    note(f"dedup byte offsets past 4 GiB: T={T} K={K} E={E} R={R} H={H}")
+    o = _gpu_dedup(dev(x), idx, E, R)
+    # rank masks and recv rows: for each rank, its tokens in token order
+    mask = np.zeros(T, np.int64)
+    for k in range(K):
+        mask |= 1 << (idx[:, k] // er)
+    rs = np.full((T, R), -1, np.int64)
+    recv_src = []
+    base = 0
+    for r in range(R):
+        toks = np.nonzero(mask & (1 << r))[0]
+        rs[toks, r] = base + np.arange(len(toks))
+        recv_src.append(toks)
+        base += len(toks)
+    recv_src = np.concatenate(recv_src)
+    n_recv = base
+    assert n_recv * H * 4 > (1 << 32)
+    np.testing.assert_array_equal(host(o.rank_slot), rs.astype(np.int32))
+    np.testing.assert_array_equal(host(o.recv_src)[:n_recv], recv_src.astype(np.int32))
+    order = np.argsort(idx.ravel(), kind="stable")
+    tm = np.empty(T * K, np.int64)
+    tm[order] = np.arange(T * K)
+    np.testing.assert_array_equal(host(o.tok_map).ravel(), tm)
+    np.testing.assert_array_equal(host(o.stats), np.zeros(3, np.int32))
+    for buf, src, n in ((o.recv_x, recv_src, n_recv), (o.packed, order // K, T * K)):
+        rows = np.unique(np.concatenate([np.arange(n - 1500, n), rng.integers(0, n, 1500)]))
+        got = host(buf[torch.from_numpy(rows).to(DEV)])
+        np.testing.assert_array_equal(got.view(np.uint32), x[src[rows]].view(np.uint32))
+    # combines of sampled tokens, the last ones included
+    w = rng.random((T, K)).astype(np.float32)
+    toks = np.unique(np.concatenate([np.arange(T - 1000, T), rng.integers(0, T, 1000)]))
+    sub_rows = np.unique(tm.reshape(T, K)[toks].ravel())
+    lookup = np.full(T * K, -1, np.int64)
+    lookup[sub_rows] = np.arange(len(sub_rows))
+    sub_tm = lookup[tm.reshape(T, K)[toks]]
+    y_sub = x[(order // K)[sub_rows]]           # the identity expert: packed rows are x rows
+    eo, ew, _ = oracle.dedup_combine(y_sub, "f32", sub_tm, w[toks], idx[toks], E, R,
+                                     rs[toks].astype(np.int32), (1 << 31) - 1, "f32")
+    rr = T * min(K, R)
+    for with_partial in (False, True):
+        part = torch.empty((rr, H), dtype=torch.float32, device=DEV) if with_partial else None
+        plan = dict(R=R, idx=dev(idx), rank_slot=o.rank_slot, recv_rows=rr, partial=part)
+        out, ow = moe.combine(o.packed, o.tok_map, dev(w), E=E, out_dtype=torch.float32,
+                              dedup=plan)
+        torch.cuda.synchronize()
+        _check_combine(host(out[torch.from_numpy(toks).to(DEV)]), eo, "f32")
+        np.testing.assert_array_equal(host(ow)[toks], ew)
+        del part, out
+
+
 # ---------------------------------------------------------------------------
 # one-launch routing: the arrival ticket lives in the caller's workspace
 # ---------------------------------------------------------------------------
