@@ -80,3 +80,42 @@ def test_noalloc_at_the_static_workspace_limit():
         note(f"noalloc limit T={T} K={K} E={E} H={H}")
         _both(x, idx, E, 0, T * K, False, False)
     assert moe.workspace_size(104641, 8, 256) > 4 << 20
+
+
+def test_noalloc_dispatch_captured_in_a_graph():
+    """The callers it is for include code under graph capture: a captured
+    moe_dispatch_noalloc, replayed three times with eager calls on other
+    inputs in between, writes what moe_dispatch writes on the same input."""
+    rng = np.random.default_rng(9)
+    T, K, E, H = 1500, 8, 64, 512
+    idx_a, idx_b = _idx(rng, T, K, E), _idx(rng, 700, K, E)
+    xa = dev_bf16(W.normal_x(rng, T, H, "bf16"))
+    xb = dev_bf16(W.normal_x(rng, 700, H, "bf16"))
+    ia, ib = dev(idx_a), dev(idx_b)
+    # rows past the valid entries are never written: both outputs start poisoned
+    ref = moe._lib.alloc_dispatch(T, H, K, E, T * K, xa.dtype, True, DEV)
+    for t in (ref.packed, ref.scales, ref.packed_src, ref.tok_map, ref.packed_cnt, ref.packed_off,
+              ref.stats):
+        poison_(t)
+    moe.dispatch(xa, ia, E, fp8=True, out=ref)
+    o = moe._lib.alloc_dispatch(T, H, K, E, T * K, xa.dtype, True, DEV)
+    moe.dispatch_noalloc(xa, ia, E, fp8=True, out=o)      # the first call on the device, eager
+    torch.cuda.synchronize()
+    note("noalloc graph capture")
+    cs = torch.cuda.Stream(DEV)
+    cs.wait_stream(torch.cuda.current_stream(DEV))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cs):
+        with torch.cuda.graph(g, stream=cs):
+            moe.dispatch_noalloc(xa, ia, E, fp8=True, out=o)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in (o.packed, o.scales, o.packed_src, o.tok_map, o.packed_cnt, o.packed_off, o.stats):
+            poison_(t)
+        g.replay()
+        torch.cuda.synchronize()
+        for name in ("tok_map", "packed_cnt", "packed_off", "packed_src", "stats", "packed"):
+            assert torch.equal(getattr(o, name), getattr(ref, name)), (rep, name)
+        assert torch.equal(o.scales.view(torch.int32), ref.scales.view(torch.int32)), rep
+        moe.dispatch_noalloc(xb, ib, E, fp8=True)          # eager work on the same array between replays
+        torch.cuda.synchronize()
