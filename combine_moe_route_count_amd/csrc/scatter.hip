@@ -533,13 +533,15 @@ int copy_threads(int nvec) {
     return th;
 }
 
+// Launch<DMAX, VPT>::go(a, s) with the smallest DMAX (destinations per source
+// row the kernel is compiled for) that holds D; each launch sizes its own grid.
 template <template <int, int> class Launch, int VPT, class Args>
-hipError_t by_dmax(int D, dim3 grid, int threads, const Args& a, hipStream_t s) {
-    if (D <= 2) Launch<2, VPT>::go(grid, threads, a, s);
-    else if (D <= 4) Launch<4, VPT>::go(grid, threads, a, s);
-    else if (D <= 8) Launch<8, VPT>::go(grid, threads, a, s);
-    else if (D <= 16) Launch<16, VPT>::go(grid, threads, a, s);
-    else Launch<32, VPT>::go(grid, threads, a, s);
+hipError_t by_dmax(int D, const Args& a, hipStream_t s) {
+    if (D <= 2) Launch<2, VPT>::go(a, s);
+    else if (D <= 4) Launch<4, VPT>::go(a, s);
+    else if (D <= 8) Launch<8, VPT>::go(a, s);
+    else if (D <= 16) Launch<16, VPT>::go(a, s);
+    else Launch<32, VPT>::go(a, s);
     return hipGetLastError();
 }
 
@@ -609,7 +611,7 @@ template <bool REPLAY, bool SC>
 struct CopyMode {
     template <int D, int V>
     struct Launch {
-        static void go(dim3, int, const ScatterArgs& a, hipStream_t s) {
+        static void go(const ScatterArgs& a, hipStream_t s) {
             const CopySplit sp = copy_split((int)(a.H * a.x_bytes / 16), kCopyChunks, kCopyWgsPerCu);
             scatter_copy_kernel<D, V, REPLAY, SC>
                 <<<copy_grid(a.T * sp.nch), dim3(sp.threads), sp.lds, s>>>(a, sp.threads, sp.nch, sp.C);
@@ -620,7 +622,7 @@ template <bool REPLAY, bool FP4>
 struct Fp8Mode {
     template <int D, int V>
     struct Launch {
-        static void go(dim3, int, const ScatterArgs& a, hipStream_t s) {
+        static void go(const ScatterArgs& a, hipStream_t s) {
             const Fp8Split sp = fp8_split(a.H, FP4);
             const int64_t items = a.T * sp.nch;
             const dim3 grid((unsigned)(items < kMaxGrid ? items : kMaxGrid));
@@ -631,7 +633,7 @@ struct Fp8Mode {
 };
 template <int D, int V>
 struct LaunchRecv {
-    static void go(dim3, int, const RecvArgs& a, hipStream_t s) {
+    static void go(const RecvArgs& a, hipStream_t s) {
         const CopySplit sp = copy_split((int)(a.H * a.x_bytes / 16), kRecvChunks, kRecvWgsPerCu);
         recv_copy_kernel<D, V>
             <<<copy_grid(a.T * sp.nch), dim3(sp.threads), sp.lds, s>>>(a, sp.threads, sp.nch, sp.C);
@@ -639,7 +641,7 @@ struct LaunchRecv {
 };
 template <int D, int V>
 struct LaunchExpand {
-    static void go(dim3, int, const ExpandArgs& a, hipStream_t s) {
+    static void go(const ExpandArgs& a, hipStream_t s) {
         const CopySplit sp = copy_split((int)(a.H * a.x_bytes / 16), kExpandChunks, kExpandWgsPerCu);
         expand_kernel<D, V><<<copy_grid(a.recv_rows * sp.nch), dim3(sp.threads), sp.lds, s>>>(
             a, sp.threads, sp.nch, sp.C);
@@ -650,23 +652,20 @@ struct LaunchExpand {
 
 hipError_t launch_scatter(const ScatterArgs& a, hipStream_t s) {
     if (a.T == 0) return hipSuccess;
-    const dim3 grid((unsigned)(a.T < kMaxGrid ? a.T : kMaxGrid));
+    const int K = a.slot.K;
     if (a.fp8) {
-        const int th = 0;   // Fp8Mode sizes its own launch (fp8_split)
         if (a.fp4)
-            return a.replay ? by_dmax<Fp8Mode<true, true>::Launch, 2>(a.slot.K, grid, th, a, s)
-                            : by_dmax<Fp8Mode<false, true>::Launch, 2>(a.slot.K, grid, th, a, s);
-        return a.replay ? by_dmax<Fp8Mode<true, false>::Launch, 2>(a.slot.K, grid, th, a, s)
-                        : by_dmax<Fp8Mode<false, false>::Launch, 2>(a.slot.K, grid, th, a, s);
+            return a.replay ? by_dmax<Fp8Mode<true, true>::Launch, 2>(K, a, s)
+                            : by_dmax<Fp8Mode<false, true>::Launch, 2>(K, a, s);
+        return a.replay ? by_dmax<Fp8Mode<true, false>::Launch, 2>(K, a, s)
+                        : by_dmax<Fp8Mode<false, false>::Launch, 2>(K, a, s);
     }
-    const int nvec = (int)(a.H * a.x_bytes / 16);
-    const int th = copy_threads<4>(nvec);
     const bool sc = a.x_scales != nullptr;
     if (a.replay)
-        return sc ? by_dmax<CopyMode<true, true>::Launch, 4>(a.slot.K, grid, th, a, s)
-                  : by_dmax<CopyMode<true, false>::Launch, 4>(a.slot.K, grid, th, a, s);
-    return sc ? by_dmax<CopyMode<false, true>::Launch, 4>(a.slot.K, grid, th, a, s)
-              : by_dmax<CopyMode<false, false>::Launch, 4>(a.slot.K, grid, th, a, s);
+        return sc ? by_dmax<CopyMode<true, true>::Launch, 4>(K, a, s)
+                  : by_dmax<CopyMode<true, false>::Launch, 4>(K, a, s);
+    return sc ? by_dmax<CopyMode<false, true>::Launch, 4>(K, a, s)
+              : by_dmax<CopyMode<false, false>::Launch, 4>(K, a, s);
 }
 
 bool dispatch_small_fits(int64_t T, int K, int E) {
@@ -688,16 +687,12 @@ hipError_t launch_dispatch_small(const ScatterArgs& a, const ScanArgs& sc, hipSt
 
 hipError_t launch_recv_copy(const RecvArgs& a, hipStream_t s) {
     if (a.T == 0) return hipSuccess;
-    const int nvec = (int)(a.H * a.x_bytes / 16);
-    const dim3 grid((unsigned)(a.T < kMaxGrid ? a.T : kMaxGrid));
-    return by_dmax<LaunchRecv, 4>(a.R, grid, copy_threads<4>(nvec), a, s);
+    return by_dmax<LaunchRecv, 4>(a.R, a, s);
 }
 
 hipError_t launch_expand(const ExpandArgs& a, hipStream_t s) {
     if (a.T == 0 || a.recv_rows == 0) return hipSuccess;
-    const int nvec = (int)(a.H * a.x_bytes / 16);
-    const dim3 grid((unsigned)(a.recv_rows < kMaxGrid ? a.recv_rows : kMaxGrid));
-    return by_dmax<LaunchExpand, 4>(a.slot.K, grid, copy_threads<4>(nvec), a, s);
+    return by_dmax<LaunchExpand, 4>(a.slot.K, a, s);
 }
 
 hipError_t launch_fp8_dequant(const uint8_t* q, const float* scales, int64_t rows, int64_t H,
