@@ -87,22 +87,33 @@ def _check(status: int) -> None:
         raise MoeError(status, load().moe_last_error().decode())
 
 
+# The marshalling below runs on every call, and decode-sized calls take a few
+# microseconds on the GPU: pointers go to ctypes as plain ints, and the current
+# stream comes from torch's raw-handle query where it exists (the public
+# Stream object costs about a microsecond more per call).
 def ptr(t: Optional[torch.Tensor]):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else t.data_ptr()
 
 
-def _stream(device) -> ctypes.c_void_p:
-    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream(device):
+    if _raw_stream is not None:
+        index = device.index if isinstance(device, torch.device) else None
+        return _raw_stream(torch.cuda.current_device() if index is None else index)
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+_DTYPE_CODES = {torch.bfloat16: MOE_BF16, torch.float32: MOE_F32, torch.uint8: MOE_FP8_E4M3,
+                torch.float8_e4m3fn: MOE_FP8_E4M3}
 
 
 def dtype_code(dt: torch.dtype) -> int:
-    if dt == torch.bfloat16:
-        return MOE_BF16
-    if dt == torch.float32:
-        return MOE_F32
-    if dt in (torch.uint8, torch.float8_e4m3fn):
-        return MOE_FP8_E4M3
-    raise ValueError(f"unsupported dtype {dt}")
+    code = _DTYPE_CODES.get(dt)
+    if code is None:
+        raise ValueError(f"unsupported dtype {dt}")
+    return code
 
 
 def version() -> int:
