@@ -188,3 +188,54 @@ def test_nonfinite_rows_through_dispatch_dequant_and_combine():
                              d["tok_map"], w, "f32")
     assert out[0, 3] == 448.0 and out[1, 130] == -448.0 and np.isnan(out[2, 7])
     assert np.isfinite(np.delete(out[2], 7)).all()
+
+
+def _f32_rne_exact(q):
+    """Round a Fraction to the nearest float32, ties to even, in exact rational
+    arithmetic (normal and subnormal results; |q| well inside the f32 range)."""
+    from fractions import Fraction
+    if q == 0:
+        return np.float32(0.0)
+    sign = -1 if q < 0 else 1
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1                                   # now 2^e <= a < 2^(e+1)
+    e = max(e, -126)                             # subnormals share the 2^-149 step
+    ulp = Fraction(2) ** (e - 23)
+    m, rem = divmod(a, ulp)
+    if rem > ulp / 2 or (rem == ulp / 2 and m % 2 == 1):
+        m += 1
+    return np.float32(sign * float(m * ulp))     # m * ulp is exact in float32
+
+
+def test_fp8_scaled_codes_against_exact_rational_quotients():
+    """The scaled branch encodes the correctly rounded f32 value of the exact
+    quotient x*448/amax: computed here with fractions and an exact rounding to
+    float32, then torch's e4m3 encoder, for blocks whose amax ranges from just
+    above 448 to the bf16 maximum (where x*448 itself exceeds the f32 range)."""
+    from fractions import Fraction
+    import torch
+    rng = np.random.default_rng(17)
+    rows = []
+    for lo, hi in ((9, 12), (20, 60), (100, 120), (120, 127)):
+        for _ in range(6):
+            with np.errstate(over="ignore"):            # a draw past the f32 range is skipped
+                f = rng.standard_normal(128).astype(np.float32)
+                f *= np.float32(2.0) ** np.float32(rng.integers(lo, hi + 1))
+                f[rng.integers(0, 128)] *= np.float32(-1.9)
+            bits = W.bf16_bits_from_f32(f)
+            v = W.f32_from_bf16_bits(bits)
+            if not np.isfinite(v).all() or np.abs(v).max() <= 448:
+                continue
+            rows.append(bits)
+    x = np.stack(rows)
+    q, s = oracle.fp8_pack_rows(x)
+    xf = W.f32_from_bf16_bits(x)
+    for r in range(x.shape[0]):
+        amax = Fraction(float(np.abs(xf[r]).max()))
+        quot = np.array([_f32_rne_exact(Fraction(float(v)) * 448 / amax) for v in xf[r]], np.float32)
+        ref = torch.from_numpy(quot).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        np.testing.assert_array_equal(q[r], ref)
+        assert s[r, 0] == _f32_rne_exact(amax / 448)
+    assert (np.abs(xf).max(axis=1) > 2.0 ** 119).any()      # some blocks overflow x*448 in f32
