@@ -28,8 +28,10 @@
  * ----------------------------------------
  * Pointers named x, y, packed_x, recv_x, out, idx, tok_map, ... are DEVICE
  * pointers.  Every buffer is allocated and freed by the caller; the library
- * allocates nothing, keeps no pointer after a call returns and holds no state
- * between calls.  Work is enqueued on `stream` (a hipStream_t passed as
+ * allocates nothing, keeps no pointer to a caller's buffer after a call
+ * returns and holds no state between calls, except the static workspace of
+ * moe_dispatch_noalloc (one array per GPU, and its device address once looked
+ * up).  Work is enqueued on `stream` (a hipStream_t passed as
  * void*, NULL = the default stream) and the call returns without waiting.
  * Results are deterministic: the same inputs give the same bits, and no
  * output needs clearing between calls.
