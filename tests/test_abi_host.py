@@ -190,6 +190,24 @@ res["route"] = {
     "ws_small": [lib.moe_route_count(A, 10, 2, 4, A, A, None, WS, 0, None),
                  lib.moe_last_error().decode()],
 }
+# moe_last_error is per thread: two threads fail differently, then each reads
+# its own text after both have failed; a thread that never failed reads ""
+import threading
+bar = threading.Barrier(2)
+thr = {}
+def _fail(name, kw):
+    st = disp(**kw)[0]
+    bar.wait()
+    thr[name] = [st, lib.moe_last_error().decode()]
+def _fresh():
+    thr["fresh"] = lib.moe_last_error().decode()
+ts = [threading.Thread(target=_fail, args=("K", dict(K=0))),
+      threading.Thread(target=_fail, args=("E", dict(E=0))), threading.Thread(target=_fresh)]
+for t in ts:
+    t.start()
+for t in ts:
+    t.join()
+res["threads"] = thr
 print(json.dumps(res))
 """)
 
@@ -276,3 +294,10 @@ def test_noalloc_dispatch_argument_errors():
         want = WORKSPACE if case.startswith("too_big") else INVALID
         assert st == want and msg, (case, st, msg)
     assert "static" in _res()["noalloc"]["too_big_E256"][1]
+
+
+def test_last_error_is_per_thread():
+    t = _res()["threads"]
+    assert t["K"][0] == INVALID and "K=0" in t["K"][1], t
+    assert t["E"][0] == INVALID and "E=0" in t["E"][1], t
+    assert t["fresh"] == "", t
