@@ -636,11 +636,9 @@ def test_dispatch_graph_replays(T):
         assert_dispatch_equal(other, ref, fp8=True)
 
 
-def test_two_streams_two_workspaces():
-    """The library keeps no state between calls: two streams, each with its own
-    workspace and buffers (one a one-launch dispatch, one multi-tile, one with
-    the fp8 pack), dispatch and combine concurrently, many times over; both
-    end with the oracle's results."""
+def _concurrent_setups():
+    """Two independent callers' inputs, buffers, workspaces and streams: a
+    one-launch dispatch (bf16) and a multi-tile one with the fp8 pack."""
     cases = [(100, 8, 64, 256, False), (3000, 8, 256, 512, True)]
     setups = []
     for n, (T, K, E, H, fp8) in enumerate(cases):
@@ -664,22 +662,67 @@ def test_two_streams_two_workspaces():
                            out=torch.empty((T, H), dtype=torch.bfloat16, device=DEV),
                            ow=torch.empty(T, dtype=torch.float32, device=DEV)))
     torch.cuda.synchronize()
-    note("two streams, two workspaces")
-    for it in range(50):
-        for s_ in setups:
-            with torch.cuda.stream(s_["st"]):
-                moe.dispatch(s_["x"], s_["idx"], s_["E"], fp8=s_["fp8"], out=s_["o"], ws=s_["ws"])
-                if s_["fp8"]:
-                    moe.combine_fp8(s_["o"].packed, s_["o"].scales, s_["o"].tok_map, s_["w"],
-                                    out=s_["out"], out_weights=s_["ow"])
-                else:
-                    moe.combine(s_["o"].packed, s_["o"].tok_map, s_["w"], out=s_["out"],
-                                out_weights=s_["ow"])
-    torch.cuda.synchronize()
+    return setups
+
+
+def _round(s_):
+    with torch.cuda.stream(s_["st"]):
+        moe.dispatch(s_["x"], s_["idx"], s_["E"], fp8=s_["fp8"], out=s_["o"], ws=s_["ws"])
+        if s_["fp8"]:
+            moe.combine_fp8(s_["o"].packed, s_["o"].scales, s_["o"].tok_map, s_["w"],
+                            out=s_["out"], out_weights=s_["ow"])
+        else:
+            moe.combine(s_["o"].packed, s_["o"].tok_map, s_["w"], out=s_["out"],
+                        out_weights=s_["ow"])
+
+
+def _check_setups(setups):
     for s_ in setups:
         assert_dispatch_equal(s_["o"], s_["ref"], fp8=s_["fp8"])
         _check_combine(host(s_["out"]), s_["eo"], "bf16")
         np.testing.assert_array_equal(host(s_["ow"]), s_["ew"])
+
+
+def test_two_streams_two_workspaces():
+    """The library keeps no state between calls: two streams, each with its own
+    workspace and buffers, dispatch and combine concurrently, many times over;
+    both end with the oracle's results."""
+    setups = _concurrent_setups()
+    note("two streams, two workspaces")
+    for it in range(50):
+        for s_ in setups:
+            _round(s_)
+    torch.cuda.synchronize()
+    _check_setups(setups)
+
+
+def test_two_host_threads():
+    """The same two callers, each driven from a host thread of its own (ctypes
+    releases the GIL, so the library's host code runs concurrently): argument
+    checks, workspace carving and launches share nothing but the HIP runtime."""
+    import threading
+    setups = _concurrent_setups()
+    note("two host threads, two streams, two workspaces")
+    errors = []
+
+    def run(s_):
+        try:
+            torch.cuda.set_device(0)
+            for it in range(50):
+                _round(s_)
+            s_["st"].synchronize()
+        except Exception as e:   # reported by the main thread
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=run, args=(s_,)) for s_ in setups]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=60)
+    assert not any(t.is_alive() for t in threads), "a host thread did not finish"
+    assert not errors, errors
+    torch.cuda.synchronize()
+    _check_setups(setups)
 
 
 @pytest.mark.parametrize("nbytes", [0, 16, 4096 + 16, (1 << 20) + 48])
