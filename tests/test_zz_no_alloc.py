@@ -119,3 +119,48 @@ def test_noalloc_dispatch_captured_in_a_graph():
         assert torch.equal(o.scales.view(torch.int32), ref.scales.view(torch.int32)), rep
         moe.dispatch_noalloc(xb, ib, E, fp8=True)          # eager work on the same array between replays
         torch.cuda.synchronize()
+
+
+def test_noalloc_from_two_host_threads_on_one_stream():
+    """Two host threads share the static array through one stream (each
+    thread's current stream is the device's default stream): the stream orders
+    their calls, so each thread's outputs equal moe_dispatch of its own input."""
+    import threading
+    rng = np.random.default_rng(21)
+    K, E, H = 8, 128, 256
+    work = []
+    for T in (1800, 90):     # a multi-tile and a one-launch dispatch
+        idx = _idx(rng, T, K, E)
+        x = dev_bf16(W.normal_x(rng, T, H, "bf16"))
+        ref = moe._lib.alloc_dispatch(T, H, K, E, T * K, x.dtype, True, DEV)
+        o = moe._lib.alloc_dispatch(T, H, K, E, T * K, x.dtype, True, DEV)
+        for t in (ref.packed, ref.scales, ref.packed_src, ref.tok_map, ref.packed_cnt,
+                  ref.packed_off, ref.stats, o.packed, o.scales, o.packed_src, o.tok_map,
+                  o.packed_cnt, o.packed_off, o.stats):
+            poison_(t)
+        i = dev(idx)
+        moe.dispatch(x, i, E, fp8=True, out=ref)
+        work.append((x, i, o, ref))
+    torch.cuda.synchronize()
+    note("noalloc two host threads, one stream")
+    errors = []
+
+    def run(x, i, o):
+        try:
+            torch.cuda.set_device(0)
+            for _ in range(20):
+                moe.dispatch_noalloc(x, i, E, fp8=True, out=o)
+        except Exception as e:   # reported by the main thread
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=run, args=(x, i, o)) for x, i, o, _ in work]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=60)
+    assert not any(t.is_alive() for t in threads) and not errors, errors
+    torch.cuda.synchronize()
+    for _, _, o, ref in work:
+        for name in ("tok_map", "packed_cnt", "packed_off", "packed_src", "stats", "packed"):
+            assert torch.equal(getattr(o, name), getattr(ref, name)), name
+        assert torch.equal(o.scales.view(torch.int32), ref.scales.view(torch.int32))
