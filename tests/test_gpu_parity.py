@@ -352,6 +352,41 @@ def test_dedup_shapes(K, E, R, H):
         np.testing.assert_array_equal(host(ow), ew)
 
 
+@pytest.mark.parametrize("mode", ["local", "one_rank"])
+def test_dedup_local_routing(mode):
+    """Routings the dedup exists for: every token's experts inside one virtual
+    rank ("local": rank t mod R; "one_rank": rank 0 for all), so each token has
+    one recv row that expands to all its experts (and, for one_rank, every
+    other rank's segments stay empty)."""
+    T, K, E, R, H = 1200, 4, 64, 8, 256
+    er = E // R
+    rng = np.random.default_rng(77 if mode == "local" else 78)
+    rank = np.arange(T) % R if mode == "local" else np.zeros(T, np.int64)
+    idx = (rank[:, None] * er + np.argsort(rng.random((T, er)), axis=1)[:, :K]).astype(np.int32)
+    idx[rng.random((T, K)) < 0.05] = -1
+    x = W.normal_x(rng, T, H, "f32")
+    w = rng.random((T, K)).astype(np.float32)
+    note(f"dedup {mode} routing")
+    o = _gpu_dedup(dev(x), idx, E, R)
+    ref = oracle.dedup_dispatch(x, "f32", idx, E, R)
+    _assert_dedup_equal(o, ref)
+    assert int(ref["recv_off"][R]) == int((idx >= 0).any(axis=1).sum())   # one recv row per token
+    rr = T * min(K, R)
+    eo, ew, ep = oracle.dedup_combine(ref["packed"], "f32", ref["tok_map"], w, idx, E, R,
+                                      ref["rank_slot"], rr, "f32", want_partial=True)
+    for with_partial in (True, False):
+        part = torch.empty((rr, H), dtype=torch.float32, device=DEV) if with_partial else None
+        poison_(part)
+        plan = dict(R=R, idx=dev(idx), rank_slot=o.rank_slot, recv_rows=rr, partial=part)
+        out, ow = moe.combine(o.packed, o.tok_map, dev(w), E=E, out_dtype=torch.float32, dedup=plan)
+        torch.cuda.synchronize()
+        _check_combine(host(out), eo, "f32")
+        np.testing.assert_array_equal(host(ow), ew)
+        if with_partial:
+            n = int(ref["recv_off"][R])
+            np.testing.assert_array_equal(host(part)[:n].view(np.uint32), ep[:n].view(np.uint32))
+
+
 @pytest.mark.parametrize("T", [1, 37, 128])
 def test_dedup_one_tile(T):
     """Both routing levels of a small dedup dispatch fit one tile (T*R and T*K
