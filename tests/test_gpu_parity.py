@@ -460,6 +460,50 @@ def test_repeat_launches_bitwise_identical():
         assert torch.equal(out.view(torch.int16), out0.view(torch.int16))
 
 
+@pytest.mark.parametrize("payload,H", [("bf16", 65536), ("f32", 32768), ("fp8", 65536),
+                                       ("fp4", 65536), ("prequant", 65536)])
+def test_wide_rows(payload, H):
+    """Rows far wider than one pass of a workgroup (128 KB bf16 / f32 rows, 512
+    scale blocks): every row mover loops over passes, the e4m3 halves hold 256
+    blocks each, and the combines run 32-64 chunks per token."""
+    T, K, E = 40, 4, 16
+    rng = np.random.default_rng(H + len(payload))
+    idx = _mixed_idx(rng, T, K, E)
+    w = rng.standard_normal((T, K)).astype(np.float32)
+    note(f"wide rows {payload} H={H}")
+    if payload == "prequant":
+        x = rng.integers(0, 256, size=(T, H), dtype=np.uint8)
+        x[(x & 0x7F) == 0x7F] = 0x11                    # no NaN codes: plain comparison below
+        xs = (rng.random((T, H // 128)) * 4 + 2.0**-8).astype(np.float32)
+        o = moe._lib.alloc_dispatch(T, H, K, E, T * K, torch.uint8, True, DEV)
+        for t in (o.packed, o.scales, o.packed_src, o.tok_map, o.packed_cnt, o.packed_off, o.stats):
+            poison_(t)
+        moe.dispatch_prequant(dev(x), dev(xs), dev(idx), E, out=o)
+        torch.cuda.synchronize()
+        ref = oracle.dispatch(x, "fp8", idx, E, x_scales=xs)
+    else:
+        dt = "f32" if payload == "f32" else "bf16"
+        x = W.normal_x(rng, T, H, dt)
+        if payload in ("fp8", "fp4"):
+            x = W.inject_outliers(x, np.arange(0, T, 3), 1000.0)
+        o = gpu_dispatch(dev_x(x, dt), idx, E, fp8=payload == "fp8", fp4=payload == "fp4")
+        ref = oracle.dispatch(x, dt, idx, E, packed_dt=payload if payload in ("fp8", "fp4") else None)
+    quant = payload in ("fp8", "fp4", "prequant")
+    assert_dispatch_equal(o, ref, fp8=quant)
+    if payload in ("bf16", "f32"):
+        out, ow = moe.combine(o.packed, o.tok_map, dev(w), out_dtype=torch.bfloat16)
+        eo, ew = oracle.combine(ref["packed"], payload, ref["tok_map"], w, "bf16")
+    elif payload == "fp4":
+        out, ow = moe.combine_fp4(o.packed, o.scales, o.tok_map, dev(w))
+        eo, ew = oracle.combine_fp4(ref["packed"], ref["scales"], ref["tok_map"], w, "bf16")
+    else:
+        out, ow = moe.combine_fp8(o.packed, o.scales, o.tok_map, dev(w))
+        eo, ew = oracle.combine_fp8(ref["packed"], ref["scales"], ref["tok_map"], w, "bf16")
+    torch.cuda.synchronize()
+    _check_combine(host(out), eo, "bf16")
+    np.testing.assert_array_equal(host(ow), ew)
+
+
 def test_grid_stride_wrap_past_max_grid():
     """More tokens than the launch cap of 2^22 workgroups, so the token loops
     wrap; small rows keep it cheap.  Covers dispatch, fp8 pack and combine."""
