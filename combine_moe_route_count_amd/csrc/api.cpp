@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "moe_route.h"
@@ -384,6 +385,12 @@ MOE_API int moe_dispatch_noalloc(const void* x, moe_dtype x_dt, int64_t T, int64
                     "T=%lld K=%d E=%d needs a %zu-byte workspace, more than the %zu bytes of the "
                     "static one: use moe_dispatch with a workspace",
                     (long long)T, K, E, need, moe::kScratchBytes);
+    // A call's launches (routing, then the scatter reading the routing's results
+    // from the shared array) are enqueued as one unit: two host threads calling
+    // on one stream cannot interleave their launches, so the stream orders whole
+    // calls.  Only the enqueue is serialized; nothing waits for the device.
+    static std::mutex enqueue_mu;
+    std::lock_guard<std::mutex> lock(enqueue_mu);
     void* ws = nullptr;
     MOE_HIP(moe::scratch_for_stream((hipStream_t)stream, &ws), "moe_dispatch_noalloc workspace");
     return dispatch_impl(x, x_dt, nullptr, T, H, idx, K, E, cap, packed_rows, packed_x, packed_dt,

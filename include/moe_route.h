@@ -162,8 +162,10 @@ int moe_dispatch(const void* x, moe_dtype x_dt, int64_t T, int64_t H, const int3
  * Limit: moe_workspace_size(T, K, E, 0) <= 4 MiB (T*K up to 837120 entries at
  * E = 256, 523136 at E = 1024); larger sizes return MOE_ERR_WORKSPACE before
  * anything is enqueued.  Every moe_dispatch_noalloc call on one GPU shares the
- * array: calls that may overlap (different streams) race and must be ordered
- * by the caller; calls on one stream are ordered by it. */
+ * array: calls that may overlap on the device (different streams) race and must
+ * be ordered by the caller; calls on one stream are ordered by it, also when
+ * several host threads make them (each call's launches are enqueued as one
+ * unit, under a lock held only while enqueueing). */
 int moe_dispatch_noalloc(const void* x, moe_dtype x_dt, int64_t T, int64_t H, const int32_t* idx,
                          int K, int E, int64_t cap, int64_t packed_rows, void* packed_x,
                          moe_dtype packed_dt, float* packed_scales, int32_t* packed_cnt,

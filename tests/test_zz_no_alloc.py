@@ -122,9 +122,11 @@ def test_noalloc_dispatch_captured_in_a_graph():
 
 
 def test_noalloc_from_two_host_threads_on_one_stream():
-    """Two host threads share the static array through one stream (each
-    thread's current stream is the device's default stream): the stream orders
-    their calls, so each thread's outputs equal moe_dispatch of its own input."""
+    """Two host threads share the static array through one stream: the library
+    enqueues each call's launches as one unit, so the stream orders whole calls
+    and each thread's outputs equal moe_dispatch of its own input (without that,
+    one call's scatter could run after the other call's routing had replaced
+    its routing results in the array)."""
     import threading
     rng = np.random.default_rng(21)
     K, E, H = 8, 128, 256
@@ -145,11 +147,15 @@ def test_noalloc_from_two_host_threads_on_one_stream():
     note("noalloc two host threads, one stream")
     errors = []
 
+    shared = torch.cuda.Stream(DEV)
+    shared.wait_stream(torch.cuda.current_stream(DEV))
+
     def run(x, i, o):
         try:
             torch.cuda.set_device(0)
-            for _ in range(20):
-                moe.dispatch_noalloc(x, i, E, fp8=True, out=o)
+            with torch.cuda.stream(shared):
+                for _ in range(20):
+                    moe.dispatch_noalloc(x, i, E, fp8=True, out=o)
         except Exception as e:   # reported by the main thread
             errors.append(repr(e))
 
