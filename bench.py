@@ -64,7 +64,8 @@ def source_hash(paths):
 
 
 COMBINE_SOURCES = ["combine_moe_route_count_amd/csrc/combine.hip",
-                   "combine_moe_route_count_amd/csrc/device_common.hpp"]
+                   "combine_moe_route_count_amd/csrc/device_common.hpp",
+                   "combine_moe_route_count_amd/csrc/geometry.cpp"]
 
 
 def stored_profile(kernel_hash):
@@ -1098,6 +1099,7 @@ def main():
                    "payload": "fp8_e4m3+f32_scale_per_128" if r["fp8"] else "bf16",
                    "combine": "bf16_in_f32_acc_bf16_out", "layout": "compact",
                    "buffer_sets": args.sets,
+                   "geometry": moe.geometry(),
                    "dtypes": {"x": "bf16", "payload": "fp8_e4m3" if r["fp8"] else "bf16",
                               "scales": "f32" if r["fp8"] else None, "y": "bf16",
                               "arithmetic": "f32", "accumulate": "f32", "out": "bf16"}},

@@ -8,9 +8,9 @@ raises instead of falling back to anything else.
 from ._lib import (DedupOut, DedupPlan, DispatchOut, MoeError, combine, combine_fp4, combine_fp8,
                    copy16,
                    dedup_dispatch, dispatch, dispatch_noalloc, dispatch_prequant, dispatch_replay, fp8_dequant,
-                   load, route_count, version, workspace, workspace_size)
+                   geometry, load, route_count, version, workspace, workspace_size)
 
 __all__ = ["DedupOut", "DedupPlan", "DispatchOut", "MoeError", "combine", "combine_fp4",
            "combine_fp8", "copy16",
            "dedup_dispatch", "dispatch", "dispatch_noalloc", "dispatch_prequant", "dispatch_replay", "fp8_dequant",
-           "load", "route_count", "version", "workspace", "workspace_size"]
+           "geometry", "load", "route_count", "version", "workspace", "workspace_size"]

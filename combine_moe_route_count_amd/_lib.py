@@ -55,6 +55,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.moe_version.argtypes = []
     lib.moe_last_error.restype = ctypes.c_char_p
     lib.moe_last_error.argtypes = []
+    lib.moe_geometry.restype = ctypes.c_char_p
+    lib.moe_geometry.argtypes = []
     lib.moe_workspace_size.restype = _SZ
     lib.moe_workspace_size.argtypes = [_I64, _I32, _I32, _I32]
     lib.moe_route_count.argtypes = [_P, _I64, _I32, _I32, _P, _P, _P, _P, _SZ, _P]
@@ -118,6 +120,11 @@ def dtype_code(dt: torch.dtype) -> int:
 
 def version() -> int:
     return load().moe_version()
+
+
+def geometry() -> str:
+    """The launch geometry in use ("key=value,..."; MOE_GEOM overrides it)."""
+    return load().moe_geometry().decode()
 
 
 def workspace_size(T: int, K: int, E: int, R: int = 0) -> int:

@@ -15,7 +15,8 @@ ROOT = os.path.dirname(HERE)
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmoe_route.so")
 
-SOURCES = ["api.cpp", "route.hip", "scatter.hip", "combine.hip", "route_fused.hip", "scratch.hip"]
+SOURCES = ["api.cpp", "geometry.cpp", "route.hip", "scatter.hip", "combine.hip", "route_fused.hip",
+           "scratch.hip"]
 HEADERS = ["device_common.hpp", "internal.hpp", "route_device.hpp", "rows_device.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

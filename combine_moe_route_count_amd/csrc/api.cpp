@@ -223,7 +223,9 @@ moe::SlotArgs slot_args(void* ws, const RouteWs& L, const int32_t* idx, int K, i
 
 }  // namespace
 
-MOE_API int moe_version(void) { return (1 << 16) | 1; }
+MOE_API int moe_version(void) { return (1 << 16) | 2; }
+
+MOE_API const char* moe_geometry(void) { return moe::geometry_text(); }
 
 MOE_API const char* moe_last_error(void) { return g_last_error.c_str(); }
 

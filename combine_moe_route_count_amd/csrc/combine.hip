@@ -145,10 +145,10 @@ __device__ __forceinline__ void token_entries(const CombineArgs& a, int64_t t, i
 
 // Work decomposition: workgroup (c, t) owns units [c*C, c*C + C) of token t,
 // one lane-unit per lane, so every lane issues the loads of all K rows at
-// once and there is no second pass.  Chunks of at most kChunkUnits units keep
-// the workgroups small enough that several fit on a CU and one workgroup's
-// routing round trip overlaps with the others' gathers.
-constexpr int kChunkUnits = 256;
+// once and there is no second pass.  Chunks of at most 256 units (the
+// geometry's combine_chunk_units) keep the workgroups small enough that several
+// fit on a CU and one workgroup's routing round trip overlaps with the others'
+// gathers.
 
 struct Chunking {
     int units;   // 8-element units per row
@@ -159,7 +159,8 @@ struct Chunking {
 inline Chunking chunking(int64_t H, int unit_elems = 8) {
     Chunking ch;
     ch.units = (int)(H / unit_elems);
-    ch.nch = (ch.units + kChunkUnits - 1) / kChunkUnits;
+    const int cu = geometry().combine_chunk_units;
+    ch.nch = (ch.units + cu - 1) / cu;
     ch.C = (ch.units + ch.nch - 1) / ch.nch;
     return ch;
 }
@@ -538,13 +539,16 @@ dim3 item_grid(int64_t items) {
 // lost time under the same cap (fused dedup combine 321 -> 356 us), and so did
 // the quantized combines, whose dequantize needs the VALU latency hiding of
 // full residency (e4m3 104 -> 131 us); those launch uncapped.
-constexpr int kGatherWgsPerCu = 5;
-constexpr size_t kGatherLdsReserve = kLdsPerCu / kGatherWgsPerCu;
+// (The cap is the geometry's combine_wgs_per_cu, 5 by default.)
+inline size_t gather_lds_reserve() {
+    const int n = geometry().combine_wgs_per_cu;
+    return n > 0 ? kLdsPerCu / n : 0;
+}
 
 template <bool YF32, bool OF32, int KMAX>
 void plain_go(const CombineArgs& a, hipStream_t s) {
     const Chunking ch = chunking(a.H, unit_elems(YF32));
-    const size_t lds = YF32 ? 0 : kGatherLdsReserve;
+    const size_t lds = YF32 ? 0 : gather_lds_reserve();
     combine_kernel<YF32, OF32, KMAX>
         <<<item_grid(a.T * ch.nch), dim3(threads_for(ch.C)), lds, s>>>(a, ch.C, ch.nch);
 }

@@ -147,6 +147,24 @@ hipError_t launch_fp8_dequant(const uint8_t* q, const float* scales, int64_t row
                               void* y, hipStream_t s);
 hipError_t launch_copy16(const void* src, void* dst, int64_t bytes, hipStream_t s);
 
+// Launch geometry of the row movers and gathers (geometry.cpp): the measured
+// defaults, or the overrides of MOE_GEOM, read once.  Only how the work is split
+// over workgroups and how many share a CU; never what is computed.
+struct Geometry {
+    int combine_chunk_units;   // lane-units per combine workgroup (64..256)
+    int combine_wgs_per_cu;    // residency cap of the bf16 gather (0: none)
+    int fp8_chunks;            // workgroups per token row of the e4m3 pack
+    int fp8_wgs_per_cu;
+    int copy_chunks;           // bit-copy scatter
+    int copy_wgs_per_cu;
+    int recv_chunks;           // dedup recv copy
+    int recv_wgs_per_cu;
+    int expand_chunks;         // dedup expansion
+    int expand_wgs_per_cu;
+};
+const Geometry& geometry();
+const char* geometry_text();   // "key=value,..." (and "; ignored: ..." for rejected overrides)
+
 // The static workspace of moe_dispatch_noalloc (scratch.hip): its size, and the
 // device address of the copy on the GPU that owns stream s (looked up once per
 // GPU, with that GPU current).

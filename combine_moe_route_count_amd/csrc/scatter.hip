@@ -559,17 +559,16 @@ struct Fp8Split {
     int threads;
     size_t lds;
 };
-constexpr int kFp8SplitChunks = 2;
-constexpr int kFp8SplitWgsPerCu = 8;
 
 inline Fp8Split fp8_split(int64_t H, bool fp4) {
     const int nunits = (int)(H / 16);
     const int nblk = nunits / 8;
     Fp8Split sp;
-    sp.nch = fp4 ? 1 : (nblk < kFp8SplitChunks ? nblk : kFp8SplitChunks);
+    const int chunks = geometry().fp8_chunks, wpc = geometry().fp8_wgs_per_cu;
+    sp.nch = fp4 ? 1 : (nblk < chunks ? nblk : chunks);
     sp.C = ((nblk + sp.nch - 1) / sp.nch) * 8;
     sp.threads = copy_threads<2>(sp.C);
-    sp.lds = fp4 ? 0 : kLdsPerCu / kFp8SplitWgsPerCu;
+    sp.lds = fp4 || wpc == 0 ? 0 : kLdsPerCu / wpc;
     return sp;
 }
 
@@ -599,9 +598,6 @@ inline CopySplit copy_split(int nvec, int chunks, int wgs_per_cu) {
 // write a narrower band of the rank's expert segments (T=16384 H=4096 E=64 K=6
 // R=8: dedup dispatch 788 -> 766 us with the cap, 760 us with the split recv
 // copy; caps of 3 or 6 per CU, or chunked expansion rows, were slower).
-constexpr int kCopyChunks = 1, kCopyWgsPerCu = 0;
-constexpr int kRecvChunks = 2, kRecvWgsPerCu = 0;
-constexpr int kExpandChunks = 1, kExpandWgsPerCu = 4;
 
 inline dim3 copy_grid(int64_t items) {
     return dim3((unsigned)(items < kMaxGrid ? items : kMaxGrid));
@@ -612,7 +608,8 @@ struct CopyMode {
     template <int D, int V>
     struct Launch {
         static void go(const ScatterArgs& a, hipStream_t s) {
-            const CopySplit sp = copy_split((int)(a.H * a.x_bytes / 16), kCopyChunks, kCopyWgsPerCu);
+            const CopySplit sp = copy_split((int)(a.H * a.x_bytes / 16), geometry().copy_chunks,
+                                            geometry().copy_wgs_per_cu);
             scatter_copy_kernel<D, V, REPLAY, SC>
                 <<<copy_grid(a.T * sp.nch), dim3(sp.threads), sp.lds, s>>>(a, sp.threads, sp.nch, sp.C);
         }
@@ -634,7 +631,7 @@ struct Fp8Mode {
 template <int D, int V>
 struct LaunchRecv {
     static void go(const RecvArgs& a, hipStream_t s) {
-        const CopySplit sp = copy_split((int)(a.H * a.x_bytes / 16), kRecvChunks, kRecvWgsPerCu);
+        const CopySplit sp = copy_split((int)(a.H * a.x_bytes / 16), geometry().recv_chunks, geometry().recv_wgs_per_cu);
         recv_copy_kernel<D, V>
             <<<copy_grid(a.T * sp.nch), dim3(sp.threads), sp.lds, s>>>(a, sp.threads, sp.nch, sp.C);
     }
@@ -642,7 +639,8 @@ struct LaunchRecv {
 template <int D, int V>
 struct LaunchExpand {
     static void go(const ExpandArgs& a, hipStream_t s) {
-        const CopySplit sp = copy_split((int)(a.H * a.x_bytes / 16), kExpandChunks, kExpandWgsPerCu);
+        const CopySplit sp = copy_split((int)(a.H * a.x_bytes / 16), geometry().expand_chunks,
+                                         geometry().expand_wgs_per_cu);
         expand_kernel<D, V><<<copy_grid(a.recv_rows * sp.nch), dim3(sp.threads), sp.lds, s>>>(
             a, sp.threads, sp.nch, sp.C);
     }

@@ -102,6 +102,17 @@ int moe_version(void);
 /* Text of the calling thread's last non-OK status ("" if none). */
 const char* moe_last_error(void);
 
+/* The launch geometry in use, as "key=value,..." (a tuning aid for benchmark
+ * runs, not part of any result): workgroups per row of each row mover, lane
+ * units per combine workgroup, and the per-CU residency caps.  Defaults are the
+ * shapes measured fastest on MI355X; the environment variable MOE_GEOM, read
+ * once before the first launch, overrides them with pairs in the same form
+ * (e.g. "combine_chunk_units=224,combine_wgs_per_cu=4").  An unknown key, a
+ * malformed pair or a value outside the key's range is ignored and listed after
+ * "; ignored: ".  Results are the same bits under every accepted geometry.
+ * The string is owned by the library and lives until the process ends. */
+const char* moe_geometry(void);
+
 /* Bytes of device workspace that moe_route_count, moe_dispatch,
  * moe_dispatch_prequant and (with R > 0) moe_dedup_dispatch need for these
  * sizes (moe_dispatch_replay and the combines need none).  The workspace needs no

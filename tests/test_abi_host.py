@@ -35,6 +35,7 @@ lib = L.load()
 res = {}
 res["exports"] = {n: hasattr(lib, n) for n in NAMES}
 res["version"] = lib.moe_version()
+res["geometry"] = lib.moe_geometry().decode()
 res["ws"] = [lib.moe_workspace_size(*a) for a in [(8192, 8, 256, 0), (8192, 8, 256, 0),
              (16384, 6, 64, 8), (0, 1, 1, 0), (1, 16, 1024, 0), (-1, 8, 8, 0)]]
 P = ctypes.c_void_p
@@ -243,7 +244,7 @@ def test_workspace_size():
     assert ws[2] > 0 and ws[3] > 0 and ws[4] > 0
     assert ws[5] == 0                  # invalid sizes give 0
     assert all(w % 256 == 0 for w in ws)
-    assert _res()["version"] >> 16 == 1
+    assert _res()["version"] >> 16 == 1 and _res()["version"] & 0xFFFF >= 2
 
 
 INVALID, UNSUPPORTED, WORKSPACE = -1, -2, -3
@@ -301,3 +302,32 @@ def test_last_error_is_per_thread():
     assert t["K"][0] == INVALID and "K=0" in t["K"][1], t
     assert t["E"][0] == INVALID and "E=0" in t["E"][1], t
     assert t["fresh"] == "", t
+
+
+DEFAULT_GEOMETRY = ("combine_chunk_units=256,combine_wgs_per_cu=5,fp8_chunks=2,fp8_wgs_per_cu=8,"
+                    "copy_chunks=1,copy_wgs_per_cu=0,recv_chunks=2,recv_wgs_per_cu=0,"
+                    "expand_chunks=1,expand_wgs_per_cu=4")
+
+
+def test_default_geometry():
+    assert _res()["geometry"] == DEFAULT_GEOMETRY
+
+
+def test_geometry_override_and_rejects():
+    """MOE_GEOM overrides keys in range and lists everything else as ignored."""
+    code = ("import sys\nsys.path.insert(0, %r)\nfrom combine_moe_route_count_amd import _lib\n"
+            "print(_lib.load().moe_geometry().decode())" % ROOT)
+    env = dict(os.environ, ROCR_VISIBLE_DEVICES="-1", HIP_VISIBLE_DEVICES="-1",
+               MOE_GEOM="combine_chunk_units=224,copy_chunks=2,bogus=3,fp8_chunks=99,"
+                        "expand_wgs_per_cu=x,,combine_wgs_per_cu=0,recv_chunks,fp8_wgs_per_cu=2,"
+                        "combine_chunk_units=32")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env,
+                       timeout=120)
+    assert r.returncode == 0, r.stderr
+    got = r.stdout.strip().splitlines()[-1]
+    want = (DEFAULT_GEOMETRY.replace("combine_chunk_units=256", "combine_chunk_units=224")
+            .replace("copy_chunks=1", "copy_chunks=2")
+            .replace("combine_wgs_per_cu=5", "combine_wgs_per_cu=0")
+            + "; ignored: bogus=3,fp8_chunks=99,expand_wgs_per_cu=x,recv_chunks,fp8_wgs_per_cu=2,"
+              "combine_chunk_units=32")
+    assert got == want, got

@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CLANG = "/opt/rocm/llvm/bin/clang++"
 DEVICE_OBJECTS = ["route.hip.o", "scatter.hip.o", "combine.hip.o", "route_fused.hip.o",
-                  "scratch.hip.o"]
+                  "scratch.hip.o", "geometry.cpp.o"]
 
 
 def test_abi_host_code_under_asan_ubsan(tmp_path):
