@@ -31,7 +31,7 @@
  * allocates nothing, keeps no pointer to a caller's buffer after a call
  * returns and holds no state between calls, except the static workspace of
  * moe_dispatch_noalloc (one array per GPU, and its device address once looked
- * up).  Work is enqueued on `stream` (a hipStream_t passed as
+ * up) and the launch geometry, read once (moe_geometry).  Work is enqueued on `stream` (a hipStream_t passed as
  * void*, NULL = the default stream) and the call returns without waiting.
  * Results are deterministic: the same inputs give the same bits, and no
  * output needs clearing between calls.
