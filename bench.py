@@ -154,6 +154,11 @@ PROFILE_WORKLOADS = {
 PROFILE_RUNS = {
     "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d {d}/trace -o bench -- "
              "python bench.py --steps 10 --warmup 5 --no-cpu --no-latency",
+    # the headline pair alone: the combine kernel also serves the uniform_bf16
+    # line, so the full trace's average mixes two workloads
+    "trace_headline": "rocprofv3 --kernel-trace --stats --output-format csv -d {d}/trace_headline "
+                      "-o bench -- python bench.py --steps 30 --warmup 20 --no-cpu --no-latency "
+                      "--no-graph --no-fp --secondary none --no-dedup",
     "cal_FETCH_SIZE": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/cal_FETCH_SIZE -o copy -- "
                       "python bench.py --calibrate-copy --steps 3",
     "cal_WRITE_SIZE": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/cal_WRITE_SIZE -o copy -- "
@@ -252,7 +257,6 @@ def profile_text(prof_dir, out_dir):
     import workloads as W
     cmd = {k: v.format(d=prof_dir) for k, v in PROFILE_RUNS.items()}
     stats = list(csv.DictReader(open(os.path.join(prof_dir, "trace", "bench_kernel_stats.csv"))))
-    avg_us = {}
     out = ["# Kernel trace of a default bench.py run without the CPU leg, MI355X:",
            "#  the headline skewed_fp8 pair (T=8192 H=7168 E=256 K=8, Zipf 1.2, fp8 payload):",
            "#  3 setup dispatches + dequants, 5 warmup, 2x10 timed, 3 + 5 + 10 graph-replayed pairs",
@@ -265,12 +269,29 @@ def profile_text(prof_dir, out_dir):
            "# kernel | calls | avg us | min us | max us | % of GPU time", ""]
     for r in stats:
         k = _short_kernel(r["Name"])
-        avg_us.setdefault(k, float(r["AverageNs"]) / 1e3)
         out.append(f"{k:70s} {int(r['Calls']):5d} {float(r['AverageNs']) / 1e3:9.2f} "
                    f"{float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f} "
                    f"{float(r['Percentage']):6.2f}")
     with open(os.path.join(out_dir, "skewed_fp8_kernel_trace.txt"), "w") as fh:
         fh.write("\n".join(out) + "\n")
+    # the headline pair alone (the source of the combine's trace average)
+    hstats = list(csv.DictReader(open(os.path.join(prof_dir, "trace_headline",
+                                                   "bench_kernel_stats.csv"))))
+    head_avg = {}
+    hout = ["# Kernel trace of the headline skewed_fp8 pair alone (T=8192 H=7168 E=256 K=8, Zipf 1.2,",
+            "#  fp8 payload, bf16 expert outputs), MI355X: 3 setup dispatches + dequants, 20 warmup,",
+            "#  30 back-to-back and 2x30 event-timed pairs",
+            f"# command: {cmd['trace_headline']}",
+            f"# summary: python bench.py --profile-text {prof_dir} profiles",
+            "# kernel | calls | avg us | min us | max us | % of GPU time", ""]
+    for r in hstats:
+        k = _short_kernel(r["Name"])
+        head_avg.setdefault(k, float(r["AverageNs"]) / 1e3)
+        hout.append(f"{k:70s} {int(r['Calls']):5d} {float(r['AverageNs']) / 1e3:9.2f} "
+                    f"{float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f} "
+                    f"{float(r['Percentage']):6.2f}")
+    with open(os.path.join(out_dir, "skewed_fp8_headline_kernel_trace.txt"), "w") as fh:
+        fh.write("\n".join(hout) + "\n")
 
     def per_kernel(sub, name):
         d = collections.defaultdict(list)
@@ -286,7 +307,7 @@ def profile_text(prof_dir, out_dir):
     alg = kernel_algorithmic_bytes(W)
     lines = ["# HBM traffic per kernel dispatch from rocprofv3 counters, MI355X, one counter run per",
              "# workload and counter (kernels shared by several workloads are not mixed)", "# commands:"]
-    lines += [f"#   {cmd[k]}" for k in PROFILE_RUNS if k != "trace"]
+    lines += [f"#   {cmd[k]}" for k in PROFILE_RUNS if not k.startswith("trace")]
     lines += [f"#   python bench.py --profile-text {prof_dir} profiles",
               f"# calibration: the library's 16-byte copy of 1 GiB reads FETCH_SIZE {cf:.0f} and "
               f"WRITE_SIZE {cw:.0f};",
@@ -320,7 +341,7 @@ def profile_text(prof_dir, out_dir):
                 os.path.join(prof_dir, "cal_FETCH_SIZE", "copy_counter_collection.csv"),
                 os.path.join(prof_dir, "cal_WRITE_SIZE", "copy_counter_collection.csv"),
                 os.path.join(out_dir, "combine_skewed_fp8_pmc.json"),
-                trace_avg_us=avg_us.get(HEADLINE_COMBINE))
+                trace_avg_us=head_avg.get(HEADLINE_COMBINE))
 
 
 def _cpu_model():
@@ -1133,8 +1154,9 @@ def main():
                      "kernel_trace": ({"avg_launch_us": round(prof["trace_avg_us"], 2),
                                        "frac": round(comb_b / (prof["trace_avg_us"] * 1e-6) / 1e9
                                                      / HBM_PEAK_GBS, 4),
-                                       "source": "profiles/skewed_fp8_kernel_trace.txt "
-                                                 "(rocprofv3 kernel trace, same kernel source)"}
+                                       "source": "profiles/skewed_fp8_headline_kernel_trace.txt "
+                                                 "(rocprofv3 kernel trace of this pair alone, same "
+                                                 "kernel source)"}
                                       if prof.get("trace_avg_us") else None)},
         "secondary": sec,
         "fp8_combine": f8,

@@ -110,6 +110,6 @@ def test_committed_combine_profile_matches_the_sources(bench):
     _, comb = bench.algorithmic_bytes(8192, 7168, 8, 256, 8192 * 8, fp8=True)
     assert 1.0 <= d["traffic_bytes_per_launch"] / comb < 1.02
     assert 150 < d["trace_avg_us"] < 200
-    trace = open(os.path.join(ROOT, "profiles", "skewed_fp8_kernel_trace.txt")).read()
+    trace = open(os.path.join(ROOT, "profiles", "skewed_fp8_headline_kernel_trace.txt")).read()
     line = next(l for l in trace.splitlines() if l.startswith(bench.HEADLINE_COMBINE))
     assert abs(float(line.split()[-4]) - d["trace_avg_us"]) < 0.01
