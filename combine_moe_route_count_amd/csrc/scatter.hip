@@ -328,6 +328,24 @@ __global__ __launch_bounds__(kCopyThreads) void recv_copy_kernel(RecvArgs a, int
         recv_copy_kernel_item<DMAX, VPT>(a, t, nth, chunk_range(c, C, nvec), c == 0);
     }
 }
+
+// Recv row of work item wi (whole rows, n of them).  Workgroups go to the 8
+// XCDs round-robin in launch order; within each group of 64 items, XCD x takes
+// 8 consecutive recv rows (the items x, x+8, ..., x+56), so the rows' tokens,
+// expert ids and routing entries, neighbours in memory, are read through one
+// XCD's L2, and the rank's packed rows that XCD writes lie close together.  The
+// last n % 64 rows keep the plain order.  Measured on the dedup workload
+// (T=16384 H=4096 E=64 K=6 R=8 f32): dispatch 748-756 -> 733-743 us; with 4
+// rows per XCD 764-767 us, with 16 or 32 741-746 us.
+__device__ __forceinline__ int64_t expand_row_of(int64_t wi, int64_t n) {
+    constexpr int kRowsPerXcd = 8, kGroup = 8 * kRowsPerXcd;
+    const int64_t grouped = (n / kGroup) * kGroup;
+    if (wi >= grouped) return wi;
+    const int64_t g = wi / kGroup;
+    const int r = (int)(wi - g * kGroup);
+    return g * kGroup + (int64_t)(r % 8) * kRowsPerXcd + r / 8;
+}
+
 template <int KMAX, int VPT>
 __global__ __launch_bounds__(kCopyThreads) void expand_kernel(ExpandArgs a, int nth, int nch, int C) {
     // rows written by the recv copy: the uncapped total, clipped to recv_rows
@@ -336,8 +354,15 @@ __global__ __launch_bounds__(kCopyThreads) void expand_kernel(ExpandArgs a, int 
     const int nvec = (int)(a.H * a.x_bytes / 16);
     const int64_t items = n * nch;
     for (int64_t wi = blockIdx.x; wi < items; wi += gridDim.x) {
-        const int64_t j = wi / nch;
-        const int c = (int)(wi - j * nch);
+        int64_t j;
+        int c;
+        if (nch == 1) {
+            j = expand_row_of(wi, n);
+            c = 0;
+        } else {
+            j = wi / nch;
+            c = (int)(wi - j * nch);
+        }
         expand_kernel_item<KMAX, VPT>(a, j, nth, chunk_range(c, C, nvec), c == 0);
     }
 }
